@@ -1,0 +1,66 @@
+"""Pins of the oracle's projection GEMM and its bfloat16 rounding (CPU only)."""
+import numpy as np
+import torch
+
+from oracle import bf16, e4m3, gemm
+
+
+def test_bf16_rounding_matches_torch_on_float32_inputs():
+    # for float32 inputs torch's cast has a single rounding, so the two must agree
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal(200000) * 10.0 ** rng.integers(-6, 6, 200000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bf16.from_f64(x.astype(np.float64)), ref)
+
+
+def test_bf16_rounding_single_rounding_from_float64():
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa (1.0) wins;
+    # 1 + 2^-8 + 2^-40 is above the tie and must round up (a float32 double
+    # rounding would land on the tie and go down).
+    x = np.array([1 + 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8 + 2.0 ** -40)])
+    got = bf16.to_f32(bf16.from_f64(x)).astype(np.float64)
+    assert list(got) == [1.0, 1 + 2.0 ** -7, 1 + 2 * 2.0 ** -7, -(1 + 2.0 ** -7)]
+
+
+def test_per_tensor_quant_closed_form():
+    x = np.array([[448.0, -1.0], [0.5, 3.0]], np.float32)
+    codes, s = gemm.quantize_per_tensor(x)
+    assert s == np.float32(1.0)
+    assert codes.tolist() == [[0x7E, 0xB8], [0x30, 0x44]]
+
+
+def test_gemm_identity_and_scales():
+    rng = np.random.default_rng(22)
+    a_codes = rng.integers(0, 0x7E, size=(8, 16)).astype(np.uint8) | (rng.integers(0, 2, (8, 16)).astype(np.uint8) << 7)
+    eye = np.where(np.eye(16, dtype=bool), 0x38, 0x00).astype(np.uint8)   # 0x38 = 1.0
+    out = gemm.gemm_fp64(a_codes, np.float32(0.5), eye, np.float32(0.25))
+    assert np.array_equal(out, e4m3.decode(a_codes) * 0.125)
+
+
+def test_gemm_brute_force_small():
+    rng = np.random.default_rng(23)
+    a = rng.integers(0, 256, size=(3, 5)).astype(np.uint8)
+    b = rng.integers(0, 256, size=(5, 4)).astype(np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x10
+    b[(b & 0x7F) == 0x7F] = 0x11
+    out = gemm.gemm_fp64(a, np.float32(2.0), b, np.float32(0.5))
+    for i in range(3):
+        for j in range(4):
+            s = sum(e4m3.decode_code(a[i, k]) * e4m3.decode_code(b[k, j]) for k in range(5))
+            assert out[i, j] == s
+
+
+def test_fp32_accumulation_within_bound():
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((16, 512)).astype(np.float32)
+    w = (rng.standard_normal((512, 8)) / np.sqrt(512)).astype(np.float32)
+    xc, sx = gemm.quantize_per_tensor(x)
+    wc, sw = gemm.quantize_per_tensor(w)
+    exact = gemm.gemm_fp64(xc, sx, wc, sw)
+    acc = np.zeros((16, 8), np.float32)
+    a = e4m3.decode(xc).astype(np.float32)
+    b = e4m3.decode(wc).astype(np.float32)
+    for k in range(512):
+        acc = acc + a[:, k:k + 1] * b[k:k + 1, :]     # float32, sequential
+    acc = acc.astype(np.float64) * (float(sx) * float(sw))
+    assert np.all(np.abs(acc - exact) <= gemm.error_bound(xc, sx, wc, sw) + 1e-30)
