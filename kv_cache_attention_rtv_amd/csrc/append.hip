@@ -1,0 +1,266 @@
+// Cache upkeep: RoPE on the chunk's K, per-(token, head) e4m3 quantization of
+// K and V, and the write into the ring slots of the current chunk.
+//
+// The pages put RoPE and FP8 quantization at the moment a frame's K/V enter
+// the cache, once, and keep the cache in a circular buffer that advances by a
+// head index (page "Runway explains how it serves a 57B video model in real
+// time", fourth paragraph; page "Runway: Πώς ένα AI 57 δισ. παραμέτρων
+// παράγει βίντεο στα 24 fps", section "Από οκτώ H100 σε τέσσερις").
+//
+// One workgroup = one 64-slot tile of the ring x one KV head (256 threads).
+// Eight lanes share a token row: lane g of the row holds the element groups
+// [g*E, g*E+E) and [D/2+g*E, D/2+g*E+E), E = D/16, i.e. both halves of its
+// RoPE pairs, so the rotation needs no lane exchange and every bf16 load is
+// 8 lanes x 16 B = 128 B contiguous.  The row amax is an 8-lane DPP max.
+// K codes go straight to their row; V codes go through LDS and are written
+// transposed per tile ([d][64 slots], key order of the attention kernel's
+// matrix-core operand), 64 contiguous bytes per d-row.
+//
+// Arithmetic is fixed bit for bit: RoPE products and the sum/difference are
+// rounded separately (no contraction: this file is built with
+// -ffp-contract=off), scale = RN(amax/448), x/scale is the correctly rounded
+// quotient (div_rn), and the e4m3 conversion rounds to nearest even.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace rtv {
+namespace {
+
+constexpr int kAppendThreads = 256;
+
+__device__ __forceinline__ float dpp_max8(float x) {
+  // max over the 8 lanes of each row group: quad xor 1, quad xor 2, then the
+  // half-row mirror (lane i <-> 7-i within 8) pairs the two quads.
+  float y;
+  y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x = fmaxf(x, y);
+  y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x = fmaxf(x, y);
+  y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  return fmaxf(x, y);
+}
+
+// position of key `k` (0..63) inside a transposed V tile row
+__device__ __forceinline__ int vt_pos_of_key(int k) {
+  const int h = (k >> 2) & 1;
+  const int b = ((k >> 5) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+  return h * 32 + b;
+}
+// first key of the 4 consecutive positions 4*p4 .. 4*p4+3
+__device__ __forceinline__ int vt_key_of_pos4(int p4) {
+  const int h = p4 >> 3;
+  const int b = (p4 & 7) << 2;
+  return 32 * (b >> 4) + 8 * ((b >> 2) & 3) + 4 * h;
+}
+
+template <int D>
+__global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(AppendArgs a) {
+  constexpr int E = D / 16;          // elements per lane per half
+  constexpr int HALF = D / 2;
+  constexpr int LDS_STRIDE = D + 4;  // bytes per V row in LDS
+  __shared__ uint32_t vrow[kTileKeys * LDS_STRIDE / 4];
+
+  const int u = xcd_remap(blockIdx.x, a.n_work);
+  if (u < 0) return;
+  const int st = a.first_tile + u / a.n_heads;
+  const int h = u % a.n_heads;
+  const int64_t tile_lo = (int64_t)st * kTileKeys;
+  const int64_t lo = tile_lo > a.write_slot ? tile_lo : a.write_slot;
+  const int64_t end = a.write_slot + a.n_tokens;
+  const int64_t hi = (tile_lo + kTileKeys) < end ? (tile_lo + kTileKeys) : end;
+
+  const int tid = threadIdx.x;
+  const int g = tid & 7;
+
+  for (int pass = 0; pass < kTileKeys / (kAppendThreads / 8); ++pass) {
+    const int r = pass * (kAppendThreads / 8) + (tid >> 3);   // key row within the tile
+    const int64_t slot = tile_lo + r;
+    const bool valid = slot >= lo && slot < hi;
+    const int64_t t = valid ? slot - a.write_slot : 0;         // token within the chunk
+
+    // ---- K: load, rotate, quantize, store ------------------------------
+    float x0[E], x1[E];
+    {
+      const uint16_t* src = a.k + t * a.ldk + (int64_t)h * D;
+      if constexpr (E == 8) {
+        uint4 p0 = valid ? *(const uint4*)(src + g * E) : make_uint4(0, 0, 0, 0);
+        uint4 p1 = valid ? *(const uint4*)(src + HALF + g * E) : make_uint4(0, 0, 0, 0);
+        const uint32_t w0[4] = {p0.x, p0.y, p0.z, p0.w};
+        const uint32_t w1[4] = {p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x0[2 * i] = bf16_lo(w0[i]); x0[2 * i + 1] = bf16_hi(w0[i]);
+          x1[2 * i] = bf16_lo(w1[i]); x1[2 * i + 1] = bf16_hi(w1[i]);
+        }
+      } else {
+        uint2 p0 = valid ? *(const uint2*)(src + g * E) : make_uint2(0, 0);
+        uint2 p1 = valid ? *(const uint2*)(src + HALF + g * E) : make_uint2(0, 0);
+        const uint32_t w0[2] = {p0.x, p0.y};
+        const uint32_t w1[2] = {p1.x, p1.y};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          x0[2 * i] = bf16_lo(w0[i]); x0[2 * i + 1] = bf16_hi(w0[i]);
+          x1[2 * i] = bf16_lo(w1[i]); x1[2 * i + 1] = bf16_hi(w1[i]);
+        }
+      }
+    }
+    float r0[E], r1[E];
+    {
+      const float4* cs = (const float4*)(a.rope + (t * HALF + g * E) * 2);
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) {
+        const float4 c = valid ? cs[i] : make_float4(1.f, 0.f, 1.f, 0.f);  // (cos, sin) x 2
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float co = j ? c.z : c.x;
+          const float si = j ? c.w : c.y;
+          const int e = 2 * i + j;
+          const float a0 = x0[e] * co;
+          const float b0 = x1[e] * si;
+          const float a1 = x1[e] * co;
+          const float b1 = x0[e] * si;
+          r0[e] = a0 - b0;
+          r1[e] = a1 + b1;
+          amax = fmaxf(amax, fmaxf(fabsf(r0[e]), fabsf(r1[e])));
+        }
+      }
+      amax = dpp_max8(amax);
+      const RowQuant q = row_quant(amax);
+      if (valid) {
+        uint8_t* dst = a.kc + ((int64_t)h * a.slots_padded + slot) * D;
+        if constexpr (E == 8) {
+          uint2 c0, c1;
+          c0.x = quant4(r0[0], r0[1], r0[2], r0[3], q);
+          c0.y = quant4(r0[4], r0[5], r0[6], r0[7], q);
+          c1.x = quant4(r1[0], r1[1], r1[2], r1[3], q);
+          c1.y = quant4(r1[4], r1[5], r1[6], r1[7], q);
+          *(uint2*)(dst + g * E) = c0;
+          *(uint2*)(dst + HALF + g * E) = c1;
+        } else {
+          *(uint32_t*)(dst + g * E) = quant4(r0[0], r0[1], r0[2], r0[3], q);
+          *(uint32_t*)(dst + HALF + g * E) = quant4(r1[0], r1[1], r1[2], r1[3], q);
+        }
+        if (g == 0) a.ks[(int64_t)h * a.slots_padded + slot] = q.s;
+      }
+    }
+
+    // ---- V: load, quantize, stage row-major in LDS ----------------------
+    {
+      const uint16_t* src = a.v + t * a.ldv + (int64_t)h * D;
+      if constexpr (E == 8) {
+        uint4 p0 = valid ? *(const uint4*)(src + g * E) : make_uint4(0, 0, 0, 0);
+        uint4 p1 = valid ? *(const uint4*)(src + HALF + g * E) : make_uint4(0, 0, 0, 0);
+        const uint32_t w0[4] = {p0.x, p0.y, p0.z, p0.w};
+        const uint32_t w1[4] = {p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x0[2 * i] = bf16_lo(w0[i]); x0[2 * i + 1] = bf16_hi(w0[i]);
+          x1[2 * i] = bf16_lo(w1[i]); x1[2 * i + 1] = bf16_hi(w1[i]);
+        }
+      } else {
+        uint2 p0 = valid ? *(const uint2*)(src + g * E) : make_uint2(0, 0);
+        uint2 p1 = valid ? *(const uint2*)(src + HALF + g * E) : make_uint2(0, 0);
+        const uint32_t w0[2] = {p0.x, p0.y};
+        const uint32_t w1[2] = {p1.x, p1.y};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          x0[2 * i] = bf16_lo(w0[i]); x0[2 * i + 1] = bf16_hi(w0[i]);
+          x1[2 * i] = bf16_lo(w1[i]); x1[2 * i + 1] = bf16_hi(w1[i]);
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fmaxf(fabsf(x0[e]), fabsf(x1[e])));
+      amax = dpp_max8(amax);
+      const RowQuant q = row_quant(amax);
+      uint32_t* row = vrow + r * (LDS_STRIDE / 4);
+#pragma unroll
+      for (int i = 0; i < E / 4; ++i) {
+        row[(g * E) / 4 + i] = quant4(x0[4 * i], x0[4 * i + 1], x0[4 * i + 2], x0[4 * i + 3], q);
+        row[(HALF + g * E) / 4 + i] = quant4(x1[4 * i], x1[4 * i + 1], x1[4 * i + 2], x1[4 * i + 3], q);
+      }
+      if (valid && g == 0) a.vs[(int64_t)h * a.slots_padded + slot] = q.s;
+    }
+  }
+  __syncthreads();
+
+  // ---- V: transposed write of the tile ------------------------------------
+  // Thread block (p4, dq): positions 4*p4..4*p4+3 (4 consecutive keys) x
+  // d = 4*dq..4*dq+3; a 4x4 byte transpose turns 4 key rows into 4 d rows.
+  uint8_t* vt = a.vc + (((int64_t)h * (a.slots_padded / kTileKeys) + st) * D) * kTileKeys;
+  const bool full = (lo == tile_lo) && (hi == tile_lo + kTileKeys);
+  constexpr int kBlocks = 16 * (D / 4);
+#pragma unroll
+  for (int it = 0; it < kBlocks / kAppendThreads; ++it) {
+    const int id = it * kAppendThreads + tid;
+    const int p4 = id & 15;
+    const int dq = id >> 4;
+    const int key0 = vt_key_of_pos4(p4);
+    const uint32_t a0 = vrow[(key0 + 0) * (LDS_STRIDE / 4) + dq];
+    const uint32_t a1 = vrow[(key0 + 1) * (LDS_STRIDE / 4) + dq];
+    const uint32_t a2 = vrow[(key0 + 2) * (LDS_STRIDE / 4) + dq];
+    const uint32_t a3 = vrow[(key0 + 3) * (LDS_STRIDE / 4) + dq];
+    const uint32_t lo01 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+    const uint32_t o[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                           __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                           __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                           __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+    if (full) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *(uint32_t*)(vt + (int64_t)(4 * dq + e) * kTileKeys + 4 * p4) = o[e];
+    } else {
+      // partial tile (chunk not aligned to 64 slots): write only this chunk's keys
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t slot = tile_lo + key0 + c;
+          if (slot >= lo && slot < hi)
+            vt[(int64_t)(4 * dq + e) * kTileKeys + 4 * p4 + c] = (uint8_t)(o[e] >> (8 * c));
+        }
+    }
+  }
+}
+
+__global__ void encode_e4m3_kernel(const float* __restrict__ x, uint8_t* __restrict__ out, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i + 3 < n) {
+    const float4 v = *(const float4*)(x + i);
+    const uint32_t signs = sign_bytes4(v.x, v.y, v.z, v.w);
+    uint32_t w = cvt_fp8x2<false>(fabsf(v.x), fabsf(v.y), 0u);
+    w = cvt_fp8x2<true>(fabsf(v.z), fabsf(v.w), w);
+    *(uint32_t*)(out + i) = w | signs;
+  } else {
+    for (int64_t j = i; j < n; ++j) {
+      const float v = x[j];
+      const uint32_t w = cvt_fp8x2<false>(fabsf(v), 0.0f, 0u);
+      out[j] = (uint8_t)((w & 0x7F) | ((__float_as_uint(v) >> 31) << 7));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& args, int head_dim, hipStream_t stream) {
+  const int blocks = ((args.n_work + 7) / 8) * 8;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(append_rope_quant_kernel<128>, dim3(blocks), dim3(kAppendThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL(append_rope_quant_kernel<64>, dim3(blocks), dim3(kAppendThreads), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_e4m3(const float* x, uint8_t* out, int64_t n, hipStream_t stream) {
+  const int64_t threads = (n + 3) / 4;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(encode_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace rtv

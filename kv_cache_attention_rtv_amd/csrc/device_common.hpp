@@ -1,0 +1,100 @@
+// Device helpers shared by the library's kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rtv {
+
+constexpr int kWave = 64;
+constexpr int kTileKeys = 64;          // slots per V-transposed tile / attention key tile
+constexpr float kFp8Max = 448.0f;
+
+// ---- bf16 ---------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// round-to-nearest-even f32 -> bf16 bits (inputs are finite)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---- e4m3 ---------------------------------------------------------------
+// Two non-negative floats to two OCP E4M3FN codes (round to nearest even) in
+// the low (sel = false) or high (sel = true) half of `old`; byte 0/2 <- a.
+// Inputs are clamped to 448 first, which makes the conversion saturating.
+template <bool kHigh>
+__device__ __forceinline__ uint32_t cvt_fp8x2(float a, float b, uint32_t old) {
+  a = fminf(a, kFp8Max);
+  b = fminf(b, kFp8Max);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHigh);
+}
+
+// Correctly rounded |x| / s for s > 0 (normal), given r = RN(1/s):
+// q0 = RN(|x| r) is within one ulp of the quotient, the remainder |x| - q0 s
+// is exact with a fused multiply-add, and one corrected step gives RN(|x|/s)
+// (Markstein's theorem on division with a correctly rounded reciprocal).
+__device__ __forceinline__ float div_rn(float ax, float s, float r) {
+  float q0 = ax * r;
+  float rem = __builtin_fmaf(-q0, s, ax);
+  return __builtin_fmaf(rem, r, q0);
+}
+
+// Per-row quantization parameters: scale = RN(amax/448); the division works
+// on (|x| * pre, s * pre) with pre = 2^64 when s is tiny so that the
+// reciprocal and the remainder stay in the normal range (scaling by a power
+// of two does not change the quotient).
+struct RowQuant {
+  float s;      // stored scale
+  float ss;     // s * pre
+  float r;      // RN(1 / ss)
+  float pre;    // 1 or 2^64
+};
+
+__device__ __forceinline__ RowQuant row_quant(float amax) {
+  RowQuant q;
+  q.s = amax / kFp8Max;                     // correctly rounded f32 division
+  q.pre = (q.s < 0x1p-100f) ? 0x1p64f : 1.0f;
+  q.ss = q.s * q.pre;
+  q.r = 1.0f / q.ss;                        // correctly rounded f32 division
+  return q;
+}
+
+// e4m3 code (as 0..255 in the low byte) of x under row parameters q.
+__device__ __forceinline__ float quant_mag(float x, const RowQuant& q) {
+  return div_rn(fabsf(x) * q.pre, q.ss, q.r);
+}
+
+// sign bits of four floats -> 0x80 in each byte whose float is negative
+__device__ __forceinline__ uint32_t sign_bytes4(float a, float b, float c, float d) {
+  return ((__float_as_uint(a) >> 31) << 7) | ((__float_as_uint(b) >> 31) << 15) |
+         ((__float_as_uint(c) >> 31) << 23) | ((__float_as_uint(d) >> 31) << 31);
+}
+
+// Quantize four values of a row to four codes in one dword (byte k <- x_k).
+__device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3,
+                                           const RowQuant& q) {
+  uint32_t signs = sign_bytes4(x0, x1, x2, x3);
+  if (q.s == 0.0f) return signs;            // all-zero row: signed zeros
+  uint32_t w = cvt_fp8x2<false>(quant_mag(x0, q), quant_mag(x1, q), 0u);
+  w = cvt_fp8x2<true>(quant_mag(x2, q), quant_mag(x3, q), w);
+  return w | signs;
+}
+
+// ---- XCD-aware block order ------------------------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8).  Renumber so that each XCD walks a contiguous range of the logical
+// work list: logical = (b % 8) * ceil(n/8) + b / 8.  Returns -1 for the padding
+// blocks when n is not a multiple of 8 (the grid is rounded up to 8).
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int per = (n + 7) >> 3;
+  const int logical = (b & 7) * per + (b >> 3);
+  return logical < n ? logical : -1;
+}
+
+}  // namespace rtv

@@ -1,0 +1,51 @@
+// Launch interfaces between the host library and the kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rtv {
+
+struct AppendArgs {
+  const uint16_t* k;      // [n][H][D] bf16, row stride ldk elements
+  const uint16_t* v;
+  int64_t ldk, ldv;
+  const float* rope;      // (cos, sin) pairs of the chunk's first position: [n][D/2][2]
+  uint8_t* kc;            // layer K codes  [H][Sp][D]
+  uint8_t* vc;            // layer V codes  [H][Sp/64][D][64]
+  float* ks;              // layer K scales [H][Sp]
+  float* vs;
+  int64_t slots_padded;   // Sp
+  int64_t write_slot;     // first slot of the chunk
+  int32_t n_tokens;
+  int32_t n_heads;        // KV heads
+  int32_t first_tile;     // write_slot / 64
+  int32_t n_work;         // (#64-slot tiles touched) * n_heads
+};
+
+struct AttendArgs {
+  const uint16_t* q;      // [n][Hq][D] bf16, row stride ldq
+  uint16_t* out;          // [n][Hq][D] bf16, row stride ldo
+  int64_t ldq, ldo;
+  const float* rope;      // (cos, sin) pairs of the chunk's first position
+  const uint8_t* kc;      // layer ring (see AppendArgs)
+  const uint8_t* vc;
+  const float* ks;
+  const float* vs;
+  int64_t slots_padded;
+  int64_t seg_lo[2];      // window segments in slot space [lo, hi)
+  int64_t seg_hi[2];
+  int32_t n_segments;
+  int32_t n_tokens;
+  int32_t n_q_heads;
+  int32_t group;          // n_q_heads / n_kv_heads
+  int32_t n_qtiles;       // ceil(n_tokens / queries per workgroup)
+  int32_t n_work;         // n_qtiles * n_q_heads
+};
+
+hipError_t launch_append(const AppendArgs& args, int head_dim, hipStream_t stream);
+hipError_t launch_attend(const AttendArgs& args, int head_dim, hipStream_t stream);
+hipError_t launch_encode_e4m3(const float* x, uint8_t* out, int64_t n, hipStream_t stream);
+int attend_queries_per_block();
+
+}  // namespace rtv

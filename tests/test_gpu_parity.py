@@ -1,0 +1,196 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Bit-exact: e4m3 codes, f32 scales and ring slots.  Attention: max |err| <= 2e-2
+and mean |err| <= 2e-3 against float64 attention on the dequantized cache
+(N(0,1) workloads); the stress workload is checked normalised by the window's
+max |V| (its heavy-tailed V makes absolute errors scale with |V|).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.cache import OracleKVCache
+from oracle import e4m3 as oe4m3
+from tests.gpu_helpers import attention_errors, bf16_to_np_f32, ring_rows, to_dev_bf16, vt_key
+from workloads import get_workload, qkv_normal
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def _caches(rtv, wl, max_global_frames=None, n_layers=None):
+    steps = max(wl.steps, 1)
+    cfg = rtv.RtvConfig(
+        n_layers=n_layers or wl.n_layers, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+        head_dim=wl.head_dim, tokens_per_frame=wl.tokens_per_frame, chunk_frames=wl.chunk_frames,
+        capacity_frames=wl.capacity_frames,
+        max_global_frames=max_global_frames or (steps + 2) * wl.chunk_frames,
+        rope_base=wl.rope_base)
+    gpu = rtv.RtvCache(cfg)
+    ora = OracleKVCache(cfg.n_layers, wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame,
+                        wl.chunk_frames, wl.capacity_frames, wl.rope_base)
+    return gpu, ora
+
+
+def _check_ring(gpu, ora, layer, max_window=0):
+    """Every window token's codes/scales at its expected slot, bit for bit."""
+    frames, tok, kc, ks, vc, vs = ora.window(layer, max_window)
+    slots = ora.expected_slots(layer, max_window)
+    w = gpu.window(layer, max_window)
+    assert w.window_frames == ora.window_frames(layer, max_window)
+    seg = np.concatenate([np.arange(w.seg_start[i], w.seg_start[i] + w.seg_len[i])
+                          for i in range(w.n_segments)])
+    assert np.array_equal(np.sort(seg), np.sort(slots))
+    gk, gks, gv, gvs = ring_rows(gpu, layer, slots)
+    assert np.array_equal(gk, kc), f"K codes differ at {np.argwhere(gk != kc)[:3].tolist()}"
+    assert np.array_equal(gks.view(np.uint32), ks.view(np.uint32)), "K scales differ"
+    assert np.array_equal(gv, vc), f"V codes differ at {np.argwhere(gv != vc)[:3].tolist()}"
+    assert np.array_equal(gvs.view(np.uint32), vs.view(np.uint32)), "V scales differ"
+
+
+def test_e4m3_conversion_matches_oracle(rtv_lib):
+    top = np.array([464.0], dtype=np.float32).view(np.uint32)[0]
+    bits = np.arange(0, top, 61, dtype=np.uint32)
+    mids = ((oe4m3.POS_VALUES[:-1] + oe4m3.POS_VALUES[1:]) / 2).astype(np.float32).view(np.uint32)
+    near = (mids[:, None].astype(np.int64) + np.arange(-256, 257)[None, :]).ravel().astype(np.uint32)
+    vals = oe4m3.POS_VALUES.astype(np.float32).view(np.uint32)
+    y = np.concatenate([bits, near, vals]).view(np.float32)
+    y = np.concatenate([y, -y, np.array([448.0, 450.0, 463.9, 464.0, 1e9, -0.0], np.float32)])
+    y = y[: (len(y) // 4) * 4 + 3]                     # exercise the ragged tail
+    x = torch.from_numpy(y).cuda()
+    out = torch.empty(len(y), dtype=torch.uint8, device="cuda")
+    rtv_lib.abi.rtv_encode_e4m3(x.data_ptr(), out.data_ptr(), len(y),
+                                torch.cuda.current_stream().cuda_stream)
+    got = out.cpu().numpy()
+    want = oe4m3.encode(y)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(y[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+
+
+@pytest.mark.parametrize("group", [1, 2])
+def test_tiny_stream_wraps(rtv_lib, group):
+    """12 chunks through an 8-frame ring (6 wraps), two calls per step, head_dim 64."""
+    wl = get_workload("tiny")
+    if group == 2:
+        wl = dataclasses.replace(wl, n_q_heads=4)
+    gpu, ora = _caches(rtv_lib, wl)
+    worst = (0.0, 0.0)
+    for step in range(wl.steps):
+        for call in range(2):
+            q, k, v = qkv_normal(wl, 0, step, call)
+            print(f"tiny group={group} step={step} call={call}", flush=True)
+            gpu.append(0, to_dev_bf16(k), to_dev_bf16(v))
+            ora.append(0, k, v)
+            maxw = 0 if (step + call) % 3 else wl.chunk_frames
+            out = gpu.attend(0, to_dev_bf16(q), max_window_frames=maxw)
+            want = ora.attend(0, q, max_window_frames=maxw)
+            mx, mean = attention_errors(bf16_to_np_f32(out), want)
+            worst = (max(worst[0], mx), max(worst[1], mean))
+            assert mx <= MAX_ABS and mean <= MEAN_ABS, (step, call, mx, mean)
+        _check_ring(gpu, ora, 0)
+        _check_ring(gpu, ora, 0, wl.chunk_frames)
+        gpu.advance(0)
+        ora.advance(0)
+    print("tiny worst attention error (max, mean):", worst)
+
+
+def test_poison_outside_window_and_determinism(rtv_lib):
+    """NaN codes / scales in every slot outside the window leave the output
+    bit-identical; the same call twice gives identical bits."""
+    wl = get_workload("tiny")
+    gpu, ora = _caches(rtv_lib, wl)
+    for step in range(5):
+        q, k, v = qkv_normal(wl, 0, step, 0)
+        gpu.append(0, to_dev_bf16(k), to_dev_bf16(v))
+        if step < 4:
+            gpu.advance(0)
+    qd = to_dev_bf16(q)
+    for maxw in (4, 8):
+        ref = gpu.attend(0, qd, max_window_frames=maxw).clone()
+        again = gpu.attend(0, qd, max_window_frames=maxw)
+        assert torch.equal(ref.view(torch.int16), again.view(torch.int16))
+        w = gpu.window(0, maxw)
+        inside = np.zeros(wl.capacity_tokens + 64, dtype=bool)
+        for i in range(w.n_segments):
+            inside[w.seg_start[i]: w.seg_start[i] + w.seg_len[i]] = True
+        kc, vc, ks, vs = gpu.ring_tensors(0)
+        saved = [t.clone() for t in (kc, vc, ks, vs)]
+        out_slots = torch.as_tensor(np.nonzero(~inside[: kc.shape[1]])[0], device="cuda")
+        if out_slots.numel():
+            kc[:, out_slots, :] = 0x7F
+            ks[:, out_slots] = float("nan")
+            vs[:, out_slots] = float("nan")
+            pos_of_key = torch.as_tensor(np.argsort(vt_key(np.arange(64))), device="cuda")
+            tiles = out_slots // 64
+            pos = pos_of_key[out_slots % 64]
+            vc[:, tiles, :, pos] = 0x7F
+        got = gpu.attend(0, qd, max_window_frames=maxw)
+        assert torch.equal(ref.view(torch.int16), got.view(torch.int16)), maxw
+        for t, s in zip((kc, vc, ks, vs), saved):
+            t.copy_(s)
+
+
+def test_layer_shape_steady_state(rtv_lib):
+    """12 heads x 128, 2992 tokens/frame, 16-frame ring: 5 steps (the window
+    grows 4 -> 16 frames and the ring wraps); codes bit-exact every step,
+    attention on sampled query rows."""
+    wl = get_workload("layer")
+    gpu, ora = _caches(rtv_lib, wl, max_global_frames=8 * wl.chunk_frames)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, wl.chunk_tokens - 1],
+                                     rng.integers(0, wl.chunk_tokens, 27)]))
+    for step in range(5):
+        q, k, v = qkv_normal(wl, 0, step, 0)
+        print(f"layer step={step}", flush=True)
+        gpu.append(0, to_dev_bf16(k), to_dev_bf16(v))
+        e = ora.append(0, k, v)
+        L = gpu.layout(0)
+        slots = (L.head_frame * wl.tokens_per_frame + np.arange(wl.chunk_tokens))
+        gk, gks, gv, gvs = ring_rows(gpu, 0, slots)
+        assert np.array_equal(gk, e.k_codes) and np.array_equal(gv, e.v_codes)
+        assert np.array_equal(gks.view(np.uint32), e.k_scales.view(np.uint32))
+        assert np.array_equal(gvs.view(np.uint32), e.v_scales.view(np.uint32))
+        out = gpu.attend(0, to_dev_bf16(q))
+        if step in (0, 4):
+            want = ora.attend(0, q, rows=rows)
+            mx, mean = attention_errors(bf16_to_np_f32(out)[rows], want)
+            print(f"layer step={step} attention max={mx:.3e} mean={mean:.3e}", flush=True)
+            assert mx <= MAX_ABS and mean <= MEAN_ABS
+        gpu.advance(0)
+        ora.advance(0)
+
+
+def test_state_errors(rtv_lib):
+    wl = get_workload("tiny")
+    gpu, _ = _caches(rtv_lib, wl, max_global_frames=2 * wl.chunk_frames)
+    q, k, v = qkv_normal(wl, 0, 0, 0)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    abi = rtv_lib.abi
+    with pytest.raises(rtv_lib.RtvError) as e:
+        gpu.attend(0, qd)
+    assert e.value.status == abi.RTV_ERR_STATE
+    with pytest.raises(rtv_lib.RtvError) as e:
+        gpu.advance(0)
+    assert e.value.status == abi.RTV_ERR_STATE
+    with pytest.raises(rtv_lib.RtvError) as e:
+        gpu.append(1, kd, vd)
+    assert e.value.status == abi.RTV_ERR_INVALID_ARG
+    with pytest.raises(rtv_lib.RtvError) as e:
+        gpu.append(0, kd[:-1], vd[:-1])
+    assert e.value.status == abi.RTV_ERR_INVALID_ARG
+    gpu.append(0, kd, vd)
+    with pytest.raises(rtv_lib.RtvError) as e:
+        gpu.attend(0, qd, max_window_frames=2)
+    assert e.value.status == abi.RTV_ERR_INVALID_ARG
+    gpu.advance(0)
+    gpu.append(0, kd, vd)
+    gpu.advance(0)
+    with pytest.raises(rtv_lib.RtvError) as e:     # RoPE table holds 2 chunks
+        gpu.append(0, kd, vd)
+    assert e.value.status == abi.RTV_ERR_STATE
+    L = gpu.layout(0)
+    assert L.next_global_frame == 2 * wl.chunk_frames and L.appended == 0
