@@ -6,23 +6,26 @@
 // τέσσερις"; the cache holds RoPE-rotated e4m3 K and e4m3 V, page "Runway
 // explains how it serves a 57B video model in real time", fourth paragraph).
 //
-// Work decomposition: one workgroup = 128 queries of one query head (4 waves
-// x 32 queries), iterating over 64-key tiles of the window's (at most two)
-// slot segments.  Tiles are staged in LDS, double buffered: K rows [64][D],
-// transposed V [D][64] (key order permuted in the ring so that each lane's
-// 32 operand bytes are contiguous), and the per-key scales.
+// Work decomposition: one workgroup = 256 queries of one query head, 4 waves
+// of 64 queries, each wave two 32-query sub-tiles that share every K and V
+// operand it reads from LDS (half the LDS traffic of one sub-tile per wave).
+// The workgroup walks 64-key tiles of the window's (at most two) slot
+// segments through a 3-stage LDS ring with one barrier per tile; the global
+// loads of tile t+3 are in flight while tile t is computed.
 //
-// Per wave and tile, with v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3 -> f32):
-//   S^T[key][query] = K . Q^T       (2 key sub-tiles x D/64 k-steps)
-//   lane (hh, i) of the result holds query i and 32 keys, so the softmax
-//   row is per lane plus one exchange with lane i^32;
-//   P'[query][key] = p * sv_key * c is converted to e4m3 and fed as the
-//   B operand of O^T[d][query] += V^T . P'^T   (D/32 d sub-tiles).
-// Scores: t = S_raw * sk_key * (sq_query * log2(e) / sqrt(D)); p = exp2(t - m).
-// The running max m is lazy: it moves only when a tile's max exceeds it by
-// more than kTau (log2 units), so p <= 2^kTau, and c = 448 / (2^kTau * max sv)
-// keeps every P' inside the e4m3 range with one constant for the whole window.
-// Output: O = acc / (c * l), rounded to bf16.
+// Per wave, tile and sub-tile, with v_mfma_f32_32x32x64_f8f6f4 (e4m3, f32 acc):
+//   S^T[key][query] = K . Q^T            2 key halves x D/64 k-steps
+//   lane (hh, i) holds query i and 32 of the 64 keys: the softmax row is
+//   per lane plus one v_permlane32_swap with lane i^32;
+//   P' = p * w_key, w_key = sv_key * c, converted to e4m3, is the B operand of
+//   O^T[d][query] += V^T . P'^T          D/32 d sub-tiles.
+// Scores: the queries of a workgroup share one e4m3 scale s_q, so the whole
+// per-score scale folds into a per-key factor kf = sk * s_q * log2(e)/sqrt(D)
+// and t - m = fma(S_raw, kf, -m) is one instruction.  The running max m is
+// lazy: it moves only when a tile's max exceeds it by more than kTau (log2
+// units), so p <= 2^kTau, and c = kPmax / (2^kTau * max sv over the window)
+// keeps P' below 448 with one constant for the whole window.
+// Output O = acc / (c * l), rounded to bf16.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -34,13 +37,46 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kQPW = 32;                   // queries per wave
-constexpr int kQPB = kWaves * kQPW;        // queries per workgroup
+constexpr int kSub = 1;                     // 32-query sub-tiles per wave
+constexpr int kQPW = 32 * kSub;             // queries per wave
+constexpr int kQPB = kWaves * kQPW;         // queries per workgroup
+constexpr int kStages = 3;
 constexpr float kTau = 3.0f;
+constexpr float kPmax = 440.0f;             // bound on P' (below the e4m3 max 448)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMaskFactor = 1e30f;        // kf of a key outside the window segment
 
 __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// the same with the B operand scaled by 2^(e - 127) (E8M0 exponent e):
+// adds the low-order e4m3 part of a two-term operand
+__device__ __forceinline__ v16f mfma_fp8_bscaled(const v8i& a, const v8i& b, const v16f& c, int e) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, e);
+}
+
+// two-term e4m3 of two values: hi = e4m3(x), lo = e4m3((x - hi) * 2^kLoShift)
+// (|x - hi| <= 2^-4 |x|, so the scaled residual stays in range)
+constexpr int kLoShift = 4;
+// windows shorter than this many keys use the two-term (PRECISE) kernel
+constexpr int64_t kPreciseKeys = 8192;
+template <bool HIGH>
+__device__ __forceinline__ void split_fp8x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  constexpr float kLoMul = (float)(1 << kLoShift);
+  hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)hi, HIGH);
+  const auto h = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, HIGH);
+  lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((a - h[0]) * kLoMul, (b - h[1]) * kLoMul, (int)lo, HIGH);
+}
+
+// max over lane i and lane i^32 (the two halves of a softmax row)
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // key index held by byte p of a transposed V tile row
@@ -51,13 +87,12 @@ __device__ __forceinline__ int vt_key(int p) {
 
 template <int D>
 struct Smem {
-  static constexpr int KROW = D + 16;      // padded K row (bytes): conflict-free 16 B reads
-  static constexpr int VROW = 64 + 16;     // padded transposed-V row
+  static constexpr int KROW = D + 16;       // padded K row (bytes): conflict-free 16 B reads
+  static constexpr int VROW = 64 + 16;      // padded transposed-V row
   static constexpr int K_BYTES = 64 * KROW;
   static constexpr int V_BYTES = D * VROW;
-  static constexpr int STAGE = K_BYTES + V_BYTES + 2 * 64 * 4;
+  static constexpr int STAGE = K_BYTES + V_BYTES + 2 * 64 * 4;   // + kf, wf
 };
-
 
 // staged tile: D/4 bytes of K and of V per thread (two 16 B pieces for D=128)
 struct TileRegs {
@@ -67,18 +102,8 @@ struct TileRegs {
 
 struct TileRef {
   int tile;
-  int64_t lo, hi;     // the segment the tile belongs to
+  int lo, hi;         // the segment the tile belongs to (slot indices fit in int32)
 };
-
-__device__ __forceinline__ TileRef tile_of(int it, int t_count0, int t_first0, int t_first1,
-                                           int64_t lo0, int64_t hi0, int64_t lo1, int64_t hi1) {
-  const bool second = it >= t_count0;
-  TileRef r;
-  r.lo = second ? lo1 : lo0;
-  r.hi = second ? hi1 : hi0;
-  r.tile = second ? t_first1 + (it - t_count0) : t_first0 + it;
-  return r;
-}
 
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const uint8_t* kc,
@@ -97,59 +122,157 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const u
   r.s = tid < 128 ? src[(int64_t)t.tile * 64 + (tid & 63)] : 0.0f;
 }
 
-template <int D>
+template <int D, bool MASK>
 __device__ __forceinline__ void store_piece(uint4 kq, uint4 v, int b, uint8_t* st, bool partial,
-                                            int64_t base, int64_t lo, int64_t hi) {
+                                            int base, int lo, int hi) {
   using SM = Smem<D>;
-  *(uint4*)(st + (b / D) * SM::KROW + (b % D)) = kq;
   const int row = b / 64, col = b % 64;
-  if (partial) {
-    // zero the codes of keys outside the segment (they may hold anything)
+  if (MASK && partial) {
+    // zero the codes of keys outside the segment (they may hold anything,
+    // NaN codes included): the K row of such a key, and its V bytes
+    const int kslot = base + b / D;
+    if (!(kslot >= lo && kslot < hi)) kq = make_uint4(0, 0, 0, 0);
     uint32_t m[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       m[w] = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t slot = base + vt_key(col + 4 * w + e);
+        const int slot = base + vt_key(col + 4 * w + e);
         if (slot >= lo && slot < hi) m[w] |= 0xFFu << (8 * e);
       }
     }
     v.x &= m[0]; v.y &= m[1]; v.z &= m[2]; v.w &= m[3];
   }
+  *(uint4*)(st + (b / D) * SM::KROW + (b % D)) = kq;
   *(uint4*)(st + SM::K_BYTES + row * SM::VROW + col) = v;
 }
 
-template <int D>
+// kscale = s_q * log2(e) / sqrt(D); wscale = c
+template <int D, bool MASK>
 __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, uint8_t* st,
-                                           float cP, int tid) {
+                                           float kscale, float wscale, int tid) {
   using SM = Smem<D>;
   constexpr int LD_BYTES = D / 4;
-  const int64_t base = (int64_t)t.tile * 64;
+  const int base = t.tile * 64;
   const bool partial = t.lo > base || t.hi < base + 64;
-  store_piece<D>(r.k0, r.v0, tid * LD_BYTES, st, partial, base, t.lo, t.hi);
+  store_piece<D, MASK>(r.k0, r.v0, tid * LD_BYTES, st, partial, base, t.lo, t.hi);
   if constexpr (LD_BYTES == 32)
-    store_piece<D>(r.k1, r.v1, tid * LD_BYTES + 16, st, partial, base, t.lo, t.hi);
-  float* sk_s = (float*)(st + SM::K_BYTES + SM::V_BYTES);
-  float* sw_s = sk_s + 64;
+    store_piece<D, MASK>(r.k1, r.v1, tid * LD_BYTES + 16, st, partial, base, t.lo, t.hi);
+  float* kf = (float*)(st + SM::K_BYTES + SM::V_BYTES);
+  float* wf = kf + 64;
   if (tid < 128) {
     const int key = tid & 63;
-    const int64_t slot = base + key;
-    const bool ok = slot >= t.lo && slot < t.hi;
-    if (tid < 64) sk_s[key] = ok ? r.s : 0.0f;
-    else sw_s[key] = ok ? r.s * cP : 0.0f;
+    const int slot = base + key;
+    const bool ok = !MASK || (slot >= t.lo && slot < t.hi);
+    // a key outside the segment gets kf = kMaskFactor: its raw score is the
+    // bias -448*448 added by the masking MFMA, so t ~ -2e35 and p = 0
+    if (tid < 64) kf[key] = ok ? r.s * kscale : kMaskFactor;
+    else wf[key] = ok ? r.s * wscale : 0.0f;
   }
 }
 
-template <int D>
+__device__ __forceinline__ TileRef tile_of(int it, int t_count0, int t_first0, int t_first1,
+                                           int lo0, int hi0, int lo1, int hi1) {
+  const bool second = it >= t_count0;
+  TileRef r;
+  r.lo = second ? lo1 : lo0;
+  r.hi = second ? hi1 : hi0;
+  r.tile = second ? t_first1 + (it - t_count0) : t_first0 + it;
+  return r;
+}
+
+// t = S_raw * kf - m for the 32 keys of this lane
+__device__ __forceinline__ void scores(const v16f (&s)[2], const float* kf, int hh, float m,
+                                       float (&t)[32]) {
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int key0 = 32 * kh + 8 * g + 4 * hh;
+      const float4 k4 = *(const float4*)(kf + key0);
+      const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[16 * kh + 4 * g + e] = __builtin_fmaf(s[kh][4 * g + e], kk[e], -m);
+    }
+}
+
+// Softmax of one 32-query sub-tile over one 64-key tile: consumes the raw
+// scores, updates (m, l, O), returns the e4m3 P' operand.
+template <int NDT, bool PRECISE>
+__device__ __forceinline__ v8i softmax_tile(const v16f (&s)[2], const float* kf, const float* wf,
+                                            int hh, float& m, float& l, v16f (&o)[NDT], v8i& plo) {
+  float t[32];
+  scores(s, kf, hh, m, t);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 32; j += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(t[j], t[j + 1]));
+  mx = xhalf_max(mx);
+  // lazy rescale: only when the tile max exceeds the reference by > kTau
+  // (always on the first tile, where m = -inf makes every t = +inf)
+  if (__builtin_expect(__any(mx > kTau), 0)) {
+    scores(s, kf, hh, 0.0f, t);   // raw scaled scores
+    float raw = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) raw = __builtin_fmaxf(raw, t[j]);
+    raw = xhalf_max(raw);
+    const float m_new = __builtin_fmaxf(m, raw);
+    const float alpha = exp2f(m - m_new);           // 0 on the first tile (m = -inf)
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < NDT; ++d) o[d] *= alpha;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) t[j] -= m_new;
+    m = m_new;
+  }
+  v8i pop;
+  uint32_t prev = 0;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int key0 = 32 * kh + 8 * g + 4 * hh;
+      const float4 w4 = *(const float4*)(wf + key0);
+      const float ww[4] = {w4.x, w4.y, w4.z, w4.w};
+      float pp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(t[16 * kh + 4 * g + e]);
+        l += p;
+        pp[e] = p * ww[e];
+      }
+      if constexpr (PRECISE) {
+        uint32_t c = 0, lo = 0;
+        split_fp8x2<false>(pp[0], pp[1], c, lo);
+        split_fp8x2<true>(pp[2], pp[3], c, lo);
+        pop[4 * kh + g] = (int)c;
+        plo[4 * kh + g] = (int)lo;
+      } else {
+        uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], (int)prev, false);
+        c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], (int)c, true);
+        pop[4 * kh + g] = (int)c;
+        prev = c;
+      }
+    }
+  return pop;
+}
+
+// MASK = false: every segment boundary of the window falls on a 64-slot tile
+// boundary (the host checks), so no tile needs masking and the kernel carries
+// no masking code.  MASK = true handles any boundary.
+// PRECISE = true (short windows): Q and P' are carried as two e4m3 terms,
+// hi + 2^-kLoShift * lo, each product taking a second MFMA whose B operand is
+// scaled by 2^-kLoShift; the relative error of Q and P' drops from 2^-4 to
+// about 2^-8.  The FP8 rounding error of attention shrinks with the square
+// root of the window length, so long windows keep one e4m3 term.
+template <int D, bool MASK, bool PRECISE>
 __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
   using SM = Smem<D>;
-  constexpr int NSTEP = D / 64;            // MFMA k-steps for K.Q^T
-  constexpr int NDT = D / 32;              // 32-row d sub-tiles of O^T
-  constexpr int P = D / 4;                 // RoPE pairs per lane
-  constexpr int LD_BYTES = D / 4;          // bytes per thread per matrix per tile
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SM::STAGE];
-  __shared__ float red[kWaves];
+  constexpr int NSTEP = D / 64;             // MFMA k-steps for K.Q^T
+  constexpr int NDT = D / 32;               // 32-row d sub-tiles of O^T
+  constexpr int P = D / 4;                  // RoPE pairs per lane
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * SM::STAGE];
+  __shared__ float red[2 * kWaves];
 
   const int u = xcd_remap(blockIdx.x, a.n_work);
   if (u < 0) return;
@@ -171,28 +294,21 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
   // ---- window-wide max of the V scales -> P' scale constant c -------------
   float svmax = 0.0f;
   for (int64_t slot = a.seg_lo[0] + tid; slot < a.seg_hi[0]; slot += kThreads)
-    svmax = fmaxf(svmax, vs[slot]);
+    svmax = __builtin_fmaxf(svmax, vs[slot]);
   if (a.n_segments > 1)
     for (int64_t slot = a.seg_lo[1] + tid; slot < a.seg_hi[1]; slot += kThreads)
-      svmax = fmaxf(svmax, vs[slot]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) svmax = fmaxf(svmax, __shfl_xor(svmax, o));
-  if (lane == 0) red[wave] = svmax;
-  __syncthreads();
-  svmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float cP = svmax > 0.0f ? kFp8Max / (exp2f(kTau) * svmax) : 1.0f;
+      svmax = __builtin_fmaxf(svmax, vs[slot]);
 
-  // ---- Q prologue: RoPE, per-row e4m3, B-operand layout ------------------
-  const int q_row = qtile * kQPB + wave * kQPW + li;
-  const bool q_valid = q_row < a.n_tokens;
-  const int q_src = q_valid ? q_row : a.n_tokens - 1;
-  v8i qop[NSTEP];
-  float a_i;
-  {
-    const uint16_t* src = a.q + (int64_t)q_src * a.ldq + (int64_t)head * D;
-    const float* cs = a.rope + ((int64_t)q_src * (D / 2) + P * hh) * 2;
-    float r0[P], r1[P];
-    float amax = 0.0f;
+  // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
+  int q_rows[kSub];
+  float qamax = 0.0f;
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+    const int row = qtile * kQPB + wave * kQPW + sub * 32 + li;
+    q_rows[sub] = row;
+    const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
+    const uint16_t* src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
+    const float* cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
 #pragma unroll
     for (int j = 0; j < P; j += 8) {
       const uint4 w0 = *(const uint4*)(src + P * hh + j);
@@ -204,91 +320,133 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
         const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
         const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
         const float2 c = *(const float2*)(cs + 2 * (j + e));
-        r0[j + e] = x0 * c.x - x1 * c.y;
-        r1[j + e] = x1 * c.x + x0 * c.y;
-        amax = fmaxf(amax, fmaxf(fabsf(r0[j + e]), fabsf(r1[j + e])));
+        const float r0 = x0 * c.x - x1 * c.y;
+        const float r1 = x1 * c.x + x0 * c.y;
+        qamax = __builtin_fmaxf(qamax, __builtin_fmaxf(fabsf(r0), fabsf(r1)));
       }
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float inv = amax > 0.0f ? kFp8Max / amax : 0.0f;
-    const float sq = amax / kFp8Max;
-    // an all-zero query row gets a tiny positive factor instead of 0, so that
-    // masked keys (-inf) still give p = 0 and the valid keys uniform weights
-    a_i = fmaxf(sq * (kLog2e / sqrtf((float)D)), 1e-30f);
-    // codes: operand step s holds bytes of r0 (s = 0) and r1 (s = 1) for D=128;
-    // for D=64 one step holds r0[0..15] then r1[0..15].
-    uint32_t words[NSTEP * 8];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    qamax = __builtin_fmaxf(qamax, __shfl_xor(qamax, o));
+    svmax = __builtin_fmaxf(svmax, __shfl_xor(svmax, o));
+  }
+  if (lane == 0) {
+    red[wave] = qamax;
+    red[kWaves + wave] = svmax;
+  }
+  __syncthreads();
+  qamax = 0.0f;
+  svmax = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    qamax = __builtin_fmaxf(qamax, red[w]);
+    svmax = __builtin_fmaxf(svmax, red[kWaves + w]);
+  }
+  const float q_inv = qamax > 0.0f ? kFp8Max / qamax : 0.0f;
+  const float kscale = (qamax / kFp8Max) * (kLog2e / sqrtf((float)D));
+  const float cP = svmax > 0.0f ? kPmax / (exp2f(kTau) * svmax) : 1.0f;
+
+  // ---- Q prologue pass 2: e4m3 codes in the B-operand layout ---------------
+  // operand step s, byte b <-> d: D=128: d = 64 s + 32 hh + b; D=64: byte b < 16
+  // -> d = 16 hh + b, b >= 16 -> d = 32 + 16 hh + b - 16 (RoPE pairs stay in-lane)
+  v8i qop[kSub][NSTEP];
+  v8i qlo[kSub][NSTEP];
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+    const int row = q_rows[sub];
+    const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
+    const uint16_t* src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
+    const float* cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
+    float r0[P], r1[P];
+#pragma unroll
+    for (int j = 0; j < P; j += 8) {
+      const uint4 w0 = *(const uint4*)(src + P * hh + j);
+      const uint4 w1 = *(const uint4*)(src + D / 2 + P * hh + j);
+      const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
+      const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
+        const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
+        const float2 c = *(const float2*)(cs + 2 * (j + e));
+        r0[j + e] = (x0 * c.x - x1 * c.y) * q_inv;
+        r1[j + e] = (x1 * c.x + x0 * c.y) * q_inv;
+      }
+    }
 #pragma unroll
     for (int w = 0; w < NSTEP * 8; ++w) {
       float v[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int b = 4 * w + e;           // operand byte over all steps
-        float x;
-        if constexpr (D == 128) x = (b < 32) ? r0[b] : r1[b - 32];
-        else x = (b < 16) ? r0[b] : r1[b - 16];
-        v[e] = x * inv;
+        const int b = 4 * w + e;
+        if constexpr (D == 128) v[e] = (b < 32) ? r0[b] : r1[b - 32];
+        else v[e] = (b < 16) ? r0[b] : r1[b - 16];
       }
-      const uint32_t signs = sign_bytes4(v[0], v[1], v[2], v[3]);
-      uint32_t c = cvt_fp8x2<false>(fabsf(v[0]), fabsf(v[1]), 0u);
-      c = cvt_fp8x2<true>(fabsf(v[2]), fabsf(v[3]), c);
-      words[w] = c | signs;
+      uint32_t c = 0, lo = 0;
+      if constexpr (PRECISE) {
+        split_fp8x2<false>(v[0], v[1], c, lo);
+        split_fp8x2<true>(v[2], v[3], c, lo);
+      } else {
+        c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], (int)c, true);
+      }
+      qop[sub][w / 8][w % 8] = (int)c;
+      qlo[sub][w / 8][w % 8] = (int)lo;
     }
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s)
-#pragma unroll
-      for (int w = 0; w < 8; ++w) qop[s][w] = (int)words[8 * s + w];
   }
 
   // ---- tile schedule over the segments -------------------------------------
-  // 64-slot tiles overlapping segment s: [t_first_s, t_first_s + t_count_s)
-  const int64_t lo0 = a.seg_lo[0], hi0 = a.seg_hi[0];
-  const int64_t lo1 = a.n_segments > 1 ? a.seg_lo[1] : 0;
-  const int64_t hi1 = a.n_segments > 1 ? a.seg_hi[1] : 0;
+  const int lo0 = (int)a.seg_lo[0], hi0 = (int)a.seg_hi[0];
+  const int lo1 = a.n_segments > 1 ? (int)a.seg_lo[1] : 0;
+  const int hi1 = a.n_segments > 1 ? (int)a.seg_hi[1] : 0;
   const int t_first0 = (int)(lo0 / 64);
   const int t_count0 = hi0 > lo0 ? (int)((hi0 - 1) / 64) - t_first0 + 1 : 0;
   const int t_first1 = (int)(lo1 / 64);
   const int t_count1 = hi1 > lo1 ? (int)((hi1 - 1) / 64) - t_first1 + 1 : 0;
   const int n_it = t_count0 + t_count1;
-
-  // global -> register staging of one tile
-  TileRegs regs;
-  // ---- main loop -------------------------------------------------------------
-  v16f acc_o[NDT];
-#pragma unroll
-  for (int d = 0; d < NDT; ++d) acc_o[d] = v16f{};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
-
   auto tref = [&](int it) {
     return tile_of(it, t_count0, t_first0, t_first1, lo0, hi0, lo1, hi1);
   };
-  if (n_it > 0) {
-    load_tile<D>(regs, tref(0), kc, vc, ks, vs, tid);
-    store_tile<D>(regs, tref(0), smem, cP, tid);
-  }
-  __syncthreads();
-  for (int it = 0; it < n_it; ++it) {
-    const int stage = it & 1;
-    if (it + 1 < n_it) load_tile<D>(regs, tref(it + 1), kc, vc, ks, vs, tid);
 
-    const uint8_t* st = smem + stage * SM::STAGE;
-    const float* sk_s = (const float*)(st + SM::K_BYTES + SM::V_BYTES);
-    const float* sw_s = sk_s + 64;
-    const TileRef tr = tref(it);
-    const int64_t lo = tr.lo, hi = tr.hi;
-    const int64_t base = (int64_t)tr.tile * 64;
-    const bool partial = lo > base || hi < base + 64;
-
-    // S^T = K . Q^T for the two 32-key sub-tiles
-    v16f acc_s[2];
+  v16f acc_o[kSub][NDT];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      acc_s[sub] = v16f{};
-      const uint8_t* krow = st + (32 * sub + li) * SM::KROW;
+  for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+    for (int d = 0; d < NDT; ++d) acc_o[sub][d] = v16f{};
+  float m_run[kSub], l_run[kSub];
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+    m_run[sub] = -INFINITY;
+    l_run[sub] = 0.0f;
+  }
+
+  TileRegs regs;
+#pragma unroll
+  for (int p = 0; p < kStages - 1; ++p)
+    if (p < n_it) {
+      load_tile<D>(regs, tref(p), kc, vc, ks, vs, tid);
+      store_tile<D, MASK>(regs, tref(p), smem + p * SM::STAGE, kscale, cP, tid);
+    }
+  if (kStages - 1 < n_it) load_tile<D>(regs, tref(kStages - 1), kc, vc, ks, vs, tid);
+  __syncthreads();
+
+  int stage = 0;
+  for (int it = 0; it < n_it; ++it) {
+    const uint8_t* st = smem + stage * SM::STAGE;
+    const float* kf = (const float*)(st + SM::K_BYTES + SM::V_BYTES);
+    const float* wf = kf + 64;
+    const TileRef tr = tref(it);
+    const int base = tr.tile * 64;
+    const bool partial = MASK && (tr.lo > base || tr.hi < base + 64);
+
+    // K operands (shared by both sub-tiles)
+    v8i kop[2][NSTEP];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const uint8_t* krow = st + (32 * kh + li) * SM::KROW;
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
-        v8i kop;
         uint4 k0, k1;
         if constexpr (D == 128) {
           k0 = *(const uint4*)(krow + 64 * s + 32 * hh);
@@ -297,97 +455,91 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
           k0 = *(const uint4*)(krow + 16 * hh);
           k1 = *(const uint4*)(krow + 32 + 16 * hh);
         }
-        kop[0] = k0.x; kop[1] = k0.y; kop[2] = k0.z; kop[3] = k0.w;
-        kop[4] = k1.x; kop[5] = k1.y; kop[6] = k1.z; kop[7] = k1.w;
-        acc_s[sub] = mfma_fp8(kop, qop[s], acc_s[sub]);
+        kop[kh][s] = v8i{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w,
+                         (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+      }
+    }
+    v16f acc_s[kSub][2];
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        acc_s[sub][kh] = v16f{};
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+          acc_s[sub][kh] = mfma_fp8(kop[kh][s], qop[sub][s], acc_s[sub][kh]);
+          if constexpr (PRECISE)
+            acc_s[sub][kh] = mfma_fp8_bscaled(kop[kh][s], qlo[sub][s], acc_s[sub][kh], 127 - kLoShift);
+        }
+      }
+
+    if (partial) {
+      // keys outside the segment: add -448 * 448 to their raw scores with one
+      // MFMA per key half (A: -448 at one k position of a masked key row,
+      // B: 448 at the same k position of every query column)
+      const v8i ones = v8i{hh == 0 ? 0x7E : 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int slot = base + 32 * kh + li;
+        const bool masked = !(slot >= tr.lo && slot < tr.hi);
+        const v8i bias = v8i{(hh == 0 && masked) ? 0xFE : 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int sub = 0; sub < kSub; ++sub) acc_s[sub][kh] = mfma_fp8(bias, ones, acc_s[sub][kh]);
       }
     }
 
-    // scale by the key scales; tile max
-    float uval[32];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int key0 = 32 * sub + 8 * g4 + 4 * hh;
-        const float4 skv = *(const float4*)(sk_s + key0);
-        const float sk4[4] = {skv.x, skv.y, skv.z, skv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = acc_s[sub][4 * g4 + e] * sk4[e];
-          if (partial) {
-            const int64_t slot = base + key0 + e;
-            if (!(slot >= lo && slot < hi)) x = -INFINITY;
-          }
-          uval[16 * sub + 4 * g4 + e] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float cand = mx * a_i;            // mx is finite: every tile has a valid key
-    const bool need = cand > m_run + kTau;
-    if (__any(need)) {
-      const float m_new = fmaxf(m_run, cand);
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < NDT; ++d) acc_o[d] *= alpha;
-      m_run = m_new;
-    }
-
-    // probabilities, row sum, P' codes
-    v8i pop;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int key0 = 32 * sub + 8 * g4 + 4 * hh;
-        const float4 swv = *(const float4*)(sw_s + key0);
-        const float sw4[4] = {swv.x, swv.y, swv.z, swv.w};
-        float pp[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(uval[16 * sub + 4 * g4 + e], a_i, -m_run));
-          l_run += p;
-          pp[e] = p * sw4[e];
-        }
-        uint32_t c = cvt_fp8x2<false>(pp[0], pp[1], 0u);
-        c = cvt_fp8x2<true>(pp[2], pp[3], c);
-        pop[4 * sub + g4] = (int)c;
-      }
-
-    // O^T += V^T . P'^T
+    // softmax of sub-tile 0 (overlaps the sub-tile 1 MFMAs), then its PV with
+    // the V operands that sub-tile 1 reuses
+    v8i plo;
+    v8i pop = softmax_tile<NDT, PRECISE>(acc_s[0], kf, wf, hh, m_run[0], l_run[0], acc_o[0], plo);
+    v8i vop[NDT];
 #pragma unroll
     for (int d = 0; d < NDT; ++d) {
       const uint8_t* vrow = st + SM::K_BYTES + (32 * d + li) * SM::VROW + 32 * hh;
       const uint4 v0 = *(const uint4*)(vrow);
       const uint4 v1 = *(const uint4*)(vrow + 16);
-      v8i vop;
-      vop[0] = v0.x; vop[1] = v0.y; vop[2] = v0.z; vop[3] = v0.w;
-      vop[4] = v1.x; vop[5] = v1.y; vop[6] = v1.z; vop[7] = v1.w;
-      acc_o[d] = mfma_fp8(vop, pop, acc_o[d]);
+      vop[d] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                   (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+      acc_o[0][d] = mfma_fp8(vop[d], pop, acc_o[0][d]);
+      if constexpr (PRECISE) acc_o[0][d] = mfma_fp8_bscaled(vop[d], plo, acc_o[0][d], 127 - kLoShift);
+    }
+#pragma unroll
+    for (int sub = 1; sub < kSub; ++sub) {
+      pop = softmax_tile<NDT, PRECISE>(acc_s[sub], kf, wf, hh, m_run[sub], l_run[sub], acc_o[sub], plo);
+#pragma unroll
+      for (int d = 0; d < NDT; ++d) {
+        acc_o[sub][d] = mfma_fp8(vop[d], pop, acc_o[sub][d]);
+        if constexpr (PRECISE) acc_o[sub][d] = mfma_fp8_bscaled(vop[d], plo, acc_o[sub][d], 127 - kLoShift);
+      }
     }
 
-    if (it + 1 < n_it) store_tile<D>(regs, tref(it + 1), smem + (stage ^ 1) * SM::STAGE, cP, tid);
+    const int nst = stage + 2 >= kStages ? stage + 2 - kStages : stage + 2;
+    if (it + kStages - 1 < n_it)
+      store_tile<D, MASK>(regs, tref(it + kStages - 1), smem + nst * SM::STAGE, kscale, cP, tid);
+    if (it + kStages < n_it) load_tile<D>(regs, tref(it + kStages), kc, vc, ks, vs, tid);
     __syncthreads();
+    stage = stage + 1 == kStages ? 0 : stage + 1;
   }
 
   // ---- epilogue ----------------------------------------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float scale = 1.0f / (cP * l_tot);
-  if (q_valid) {
-    uint16_t* dst = a.out + (int64_t)q_row * a.ldo + (int64_t)head * D;
 #pragma unroll
-    for (int d = 0; d < NDT; ++d)
+  for (int sub = 0; sub < kSub; ++sub) {
+    const int row = q_rows[sub];
+    const float l_tot = xhalf_sum(l_run[sub]);
+    const float scale = 1.0f / (cP * l_tot);
+    if (row < a.n_tokens) {
+      uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * d + 8 * g4 + 4 * hh;
-        uint2 w;
-        w.x = pack_bf16x2(acc_o[d][4 * g4 + 0] * scale, acc_o[d][4 * g4 + 1] * scale);
-        w.y = pack_bf16x2(acc_o[d][4 * g4 + 2] * scale, acc_o[d][4 * g4 + 3] * scale);
-        *(uint2*)(dst + d0) = w;
-      }
+      for (int d = 0; d < NDT; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * d + 8 * g + 4 * hh;
+          uint2 w;
+          w.x = pack_bf16x2(acc_o[sub][d][4 * g + 0] * scale, acc_o[sub][d][4 * g + 1] * scale);
+          w.y = pack_bf16x2(acc_o[sub][d][4 * g + 2] * scale, acc_o[sub][d][4 * g + 3] * scale);
+          *(uint2*)(dst + d0) = w;
+        }
+    }
   }
 }
 
@@ -397,10 +549,30 @@ int attend_queries_per_block() { return kQPB; }
 
 hipError_t launch_attend(const AttendArgs& args, int head_dim, hipStream_t stream) {
   const int blocks = ((args.n_work + 7) / 8) * 8;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attend_kernel<128>, dim3(blocks), dim3(kThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL(attend_kernel<64>, dim3(blocks), dim3(kThreads), 0, stream, args);
+  bool aligned = true;
+  int64_t keys = 0;
+  for (int s = 0; s < args.n_segments; ++s) {
+    aligned = aligned && args.seg_lo[s] % 64 == 0 && args.seg_hi[s] % 64 == 0;
+    keys += args.seg_hi[s] - args.seg_lo[s];
+  }
+  const bool precise = keys < kPreciseKeys;
+  const dim3 g(blocks), b(kThreads);
+#define RTV_LAUNCH(DIM, MASK, PREC) \
+  hipLaunchKernelGGL((attend_kernel<DIM, MASK, PREC>), g, b, 0, stream, args)
+  if (head_dim == 128) {
+    if (precise) {
+      if (aligned) RTV_LAUNCH(128, false, true); else RTV_LAUNCH(128, true, true);
+    } else {
+      if (aligned) RTV_LAUNCH(128, false, false); else RTV_LAUNCH(128, true, false);
+    }
+  } else {
+    if (precise) {
+      if (aligned) RTV_LAUNCH(64, false, true); else RTV_LAUNCH(64, true, true);
+    } else {
+      if (aligned) RTV_LAUNCH(64, false, false); else RTV_LAUNCH(64, true, false);
+    }
+  }
+#undef RTV_LAUNCH
   return hipGetLastError();
 }
 

@@ -194,3 +194,30 @@ def test_state_errors(rtv_lib):
     assert e.value.status == abi.RTV_ERR_STATE
     L = gpu.layout(0)
     assert L.next_global_frame == 2 * wl.chunk_frames and L.appended == 0
+
+
+@pytest.mark.parametrize("T,F,C,D,H,Hq,steps", [
+    (100, 2, 6, 128, 2, 4, 7),      # 200-token chunks: ragged 64-slot tiles, short windows
+    (100, 2, 6, 64, 2, 2, 7),
+    (2000, 2, 6, 128, 1, 2, 5),     # 4000-token chunks: ragged tiles, windows >= 8192 keys
+])
+def test_unaligned_chunks(rtv_lib, T, F, C, D, H, Hq, steps):
+    """Chunks whose token count is not a multiple of 64: appends write partial
+    64-slot tiles and attention masks the ragged tile edges of the window."""
+    wl = dataclasses.replace(get_workload("tiny"), grid_h=1, grid_w=T, chunk_frames=F,
+                             capacity_frames=C, head_dim=D, n_kv_heads=H, n_q_heads=Hq,
+                             steps=steps)
+    gpu, ora = _caches(rtv_lib, wl)
+    for step in range(steps):
+        q, k, v = qkv_normal(wl, 0, step, 0)
+        print(f"unaligned T={T} F={F} D={D} step={step}", flush=True)
+        gpu.append(0, to_dev_bf16(k), to_dev_bf16(v))
+        ora.append(0, k, v)
+        for maxw in (0, F):
+            out = gpu.attend(0, to_dev_bf16(q), max_window_frames=maxw)
+            want = ora.attend(0, q, max_window_frames=maxw)
+            mx, mean = attention_errors(bf16_to_np_f32(out), want)
+            assert mx <= MAX_ABS and mean <= MEAN_ABS, (step, maxw, mx, mean)
+        _check_ring(gpu, ora, 0)
+        gpu.advance(0)
+        ora.advance(0)
