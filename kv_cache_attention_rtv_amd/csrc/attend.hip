@@ -274,10 +274,22 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * SM::STAGE];
   __shared__ float red[2 * kWaves];
 
-  const int u = xcd_remap(blockIdx.x, a.n_work);
-  if (u < 0) return;
-  const int head = u / a.n_qtiles;
-  const int qtile = u % a.n_qtiles;
+  // work item: a whole unit (query tile x head) or one key-range part of one
+  const int xcd = blockIdx.x & 7;
+  const int local = blockIdx.x >> 3;
+  int unit, part;
+  if (local < a.full_per_xcd) {
+    unit = xcd * a.full_per_xcd + local;
+    if (unit >= a.n_full) return;
+    part = -1;
+  } else {
+    const int j = xcd * a.parts_per_xcd + (local - a.full_per_xcd);
+    if (j >= a.n_parts) return;
+    unit = a.n_full + j / a.parts_per_unit;
+    part = j;
+  }
+  const int head = unit / a.n_qtiles;
+  const int qtile = unit % a.n_qtiles;
   const int kvh = head / a.group;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -404,9 +416,13 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
   const int t_count0 = hi0 > lo0 ? (int)((hi0 - 1) / 64) - t_first0 + 1 : 0;
   const int t_first1 = (int)(lo1 / 64);
   const int t_count1 = hi1 > lo1 ? (int)((hi1 - 1) / 64) - t_first1 + 1 : 0;
-  const int n_it = t_count0 + t_count1;
+  const int n_all = t_count0 + t_count1;
+  const int pidx = part < 0 ? 0 : part % a.parts_per_unit;
+  const int pcount = part < 0 ? 1 : a.parts_per_unit;
+  const int it_begin = (int)((int64_t)n_all * pidx / pcount);
+  const int n_it = (int)((int64_t)n_all * (pidx + 1) / pcount) - it_begin;
   auto tref = [&](int it) {
-    return tile_of(it, t_count0, t_first0, t_first1, lo0, hi0, lo1, hi1);
+    return tile_of(it_begin + it, t_count0, t_first0, t_first1, lo0, hi0, lo1, hi1);
   };
 
   v16f acc_o[kSub][NDT];
@@ -526,6 +542,22 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
   for (int sub = 0; sub < kSub; ++sub) {
     const int row = q_rows[sub];
     const float l_tot = xhalf_sum(l_run[sub]);
+    if (part >= 0) {
+      // partial result of a key range: O / c unnormalized, with (m, l)
+      const int q = wave * kQPW + sub * 32 + li;
+      float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
+      const float inv_c = 1.0f / cP;
+#pragma unroll
+      for (int d = 0; d < NDT; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * d + 8 * g + 4 * hh;
+          *(float4*)(po + d0) = make_float4(acc_o[sub][d][4 * g + 0] * inv_c, acc_o[sub][d][4 * g + 1] * inv_c,
+                                            acc_o[sub][d][4 * g + 2] * inv_c, acc_o[sub][d][4 * g + 3] * inv_c);
+        }
+      if (hh == 0) *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) = make_float2(m_run[sub], l_tot);
+      continue;
+    }
     const float scale = 1.0f / (cP * l_tot);
     if (row < a.n_tokens) {
       uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D;
@@ -543,20 +575,102 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
   }
 }
 
+// Merge the key-range parts of the split units: for each query,
+// M = max_p m_p, w_p = 2^(m_p - M), O = sum_p w_p O_p / sum_p w_p l_p.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
+  const int r = blockIdx.x;                       // split unit r
+  const int unit = a.n_full + r;
+  const int head = unit / a.n_qtiles;
+  const int qtile = unit % a.n_qtiles;
+  const int S = a.parts_per_unit;
+  const int q = threadIdx.x >> 1;                 // 2 threads per query
+  const int dh = (threadIdx.x & 1) * (D / 2);
+  const int row = qtile * kQPB + q;
+  if (q >= kQPB || row >= a.n_tokens) return;
+  const int j0 = r * S;
+  float M = -INFINITY;
+  for (int p = 0; p < S; ++p) M = fmaxf(M, a.ws_ml[((int64_t)(j0 + p) * kQPB + q) * 2]);
+  float L = 0.0f;
+  float acc[D / 2];
+#pragma unroll
+  for (int d = 0; d < D / 2; ++d) acc[d] = 0.0f;
+  for (int p = 0; p < S; ++p) {
+    const float2 ml = *(const float2*)(a.ws_ml + ((int64_t)(j0 + p) * kQPB + q) * 2);
+    const float w = exp2f(ml.x - M);
+    L += w * ml.y;
+    const float* po = a.ws_o + ((int64_t)(j0 + p) * kQPB + q) * D + dh;
+#pragma unroll
+    for (int d = 0; d < D / 2; d += 4) {
+      const float4 o = *(const float4*)(po + d);
+      acc[d] += w * o.x; acc[d + 1] += w * o.y; acc[d + 2] += w * o.z; acc[d + 3] += w * o.w;
+    }
+  }
+  const float inv = 1.0f / L;
+  uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D + dh;
+#pragma unroll
+  for (int d = 0; d < D / 2; d += 8) {
+    uint4 w;
+    w.x = pack_bf16x2(acc[d] * inv, acc[d + 1] * inv);
+    w.y = pack_bf16x2(acc[d + 2] * inv, acc[d + 3] * inv);
+    w.z = pack_bf16x2(acc[d + 4] * inv, acc[d + 5] * inv);
+    w.w = pack_bf16x2(acc[d + 6] * inv, acc[d + 7] * inv);
+    *(uint4*)(dst + d) = w;
+  }
+}
+
 }  // namespace
 
 int attend_queries_per_block() { return kQPB; }
 
-hipError_t launch_attend(const AttendArgs& args, int head_dim, hipStream_t stream) {
-  const int blocks = ((args.n_work + 7) / 8) * 8;
+// parts are bounded so that the workspace has a fixed size
+constexpr int kMaxParts = 1024;
+int attend_max_parts() { return kMaxParts; }
+size_t attend_workspace_bytes(int head_dim) {
+  return (size_t)kMaxParts * kQPB * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+hipError_t attend_capacity(int* workgroups) {
+  int dev = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  hipDeviceProp_t prop;
+  if (e == hipSuccess) e = hipGetDeviceProperties(&prop, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_kernel<128, false, false>, kThreads, 0);
+  if (e != hipSuccess) return e;
+  *workgroups = (per_cu > 0 ? per_cu : 1) * prop.multiProcessorCount;
+  return hipSuccess;
+}
+
+hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t stream) {
+  AttendArgs args = args_in;
   bool aligned = true;
   int64_t keys = 0;
+  int n_tiles = 0;
   for (int s = 0; s < args.n_segments; ++s) {
     aligned = aligned && args.seg_lo[s] % 64 == 0 && args.seg_hi[s] % 64 == 0;
     keys += args.seg_hi[s] - args.seg_lo[s];
+    if (args.seg_hi[s] > args.seg_lo[s])
+      n_tiles += (int)((args.seg_hi[s] - 1) / 64 - args.seg_lo[s] / 64 + 1);
   }
   const bool precise = keys < kPreciseKeys;
-  const dim3 g(blocks), b(kThreads);
+
+  // Schedule: whole rounds of the device's concurrent workgroups run whole
+  // windows; the remainder, which would leave most of the device idle in a
+  // last round, is split along the keys so that it fills one short round.
+  const int cap = args.capacity;
+  const int U = args.n_work;
+  int rem = cap > 0 ? U % cap : 0;
+  int S = rem > 0 ? cap / rem : 1;
+  if (S > n_tiles) S = n_tiles;
+  if ((int64_t)rem * S > kMaxParts) S = kMaxParts / (rem > 0 ? rem : 1);
+  if (S < 2 || !args.ws_o) { S = 1; rem = 0; }
+  args.n_full = U - rem;
+  args.parts_per_unit = S;
+  args.n_parts = rem * S;
+  args.full_per_xcd = (args.n_full + 7) / 8;
+  args.parts_per_xcd = (args.n_parts + 7) / 8;
+  const dim3 g(8 * (args.full_per_xcd + args.parts_per_xcd)), b(kThreads);
 #define RTV_LAUNCH(DIM, MASK, PREC) \
   hipLaunchKernelGGL((attend_kernel<DIM, MASK, PREC>), g, b, 0, stream, args)
   if (head_dim == 128) {
@@ -573,6 +687,12 @@ hipError_t launch_attend(const AttendArgs& args, int head_dim, hipStream_t strea
     }
   }
 #undef RTV_LAUNCH
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rem == 0) return e;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(rem), dim3(256), 0, stream, args);
+  else
+    hipLaunchKernelGGL(combine_kernel<64>, dim3(rem), dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

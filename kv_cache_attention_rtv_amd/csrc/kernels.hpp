@@ -40,8 +40,24 @@ struct AttendArgs {
   int32_t n_q_heads;
   int32_t group;          // n_q_heads / n_kv_heads
   int32_t n_qtiles;       // ceil(n_tokens / queries per workgroup)
-  int32_t n_work;         // n_qtiles * n_q_heads
+  int32_t n_work;         // n_qtiles * n_q_heads (units of work)
+  int32_t capacity;       // workgroups the device runs concurrently (0 = never split)
+  // schedule (filled by launch_attend): units [0, n_full) run whole windows; units [n_full, n_work) are
+  // split into parts_per_unit key ranges whose partial (O, m, l) go to the
+  // workspace and are merged by the combine kernel
+  int32_t n_full;
+  int32_t parts_per_unit;
+  int32_t full_per_xcd;
+  int32_t parts_per_xcd;
+  int32_t n_parts;
+  float* ws_o;            // [n_parts][queries per workgroup][D] f32, O / c
+  float* ws_ml;           // [n_parts][queries per workgroup][2] f32 (m, l)
 };
+
+// concurrent workgroups per device and workspace bound of the attention kernel
+int attend_max_parts();
+size_t attend_workspace_bytes(int head_dim);
+hipError_t attend_capacity(int* workgroups);
 
 hipError_t launch_append(const AppendArgs& args, int head_dim, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& args, int head_dim, hipStream_t stream);

@@ -38,7 +38,7 @@ struct LayerState {
 
 struct Plan {
   int64_t slots = 0, slots_padded = 0;
-  size_t rope_bytes = 0, codes_bytes = 0, scales_bytes = 0, layer_bytes = 0, total = 0;
+  size_t rope_bytes = 0, ws_bytes = 0, codes_bytes = 0, scales_bytes = 0, layer_bytes = 0, total = 0;
 };
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
@@ -76,13 +76,15 @@ rtv_status make_plan(const rtv_config* c, Plan* p) {
   if (!mul_ok(tmp, c->head_dim, &rope_elems)) return RTV_ERR_INVALID_ARG;   // (D/2) * 2 floats
   if (!mul_ok(rope_elems, 4, &tmp)) return RTV_ERR_INVALID_ARG;
   p->rope_bytes = align_up((size_t)tmp);
+  // attention workspace (partial results of split key ranges), shared by all layers
+  p->ws_bytes = align_up(rtv::attend_workspace_bytes(c->head_dim));
   if (!mul_ok((int64_t)c->n_kv_heads * c->head_dim, Sp, &tmp)) return RTV_ERR_INVALID_ARG;
   p->codes_bytes = align_up((size_t)tmp);
   p->scales_bytes = align_up((size_t)c->n_kv_heads * (size_t)Sp * 4);
   p->layer_bytes = 2 * p->codes_bytes + 2 * p->scales_bytes;
   int64_t layers_total;
   if (!mul_ok((int64_t)p->layer_bytes, c->n_layers, &layers_total)) return RTV_ERR_INVALID_ARG;
-  p->total = p->rope_bytes + (size_t)layers_total;
+  p->total = p->rope_bytes + p->ws_bytes + (size_t)layers_total;
   return RTV_OK;
 }
 
@@ -124,6 +126,8 @@ struct rtv_cache {
   Plan plan;
   uint8_t* base = nullptr;
   float* rope = nullptr;
+  float* ws = nullptr;          // attention workspace
+  int capacity = 0;             // concurrent attention workgroups on the device
   std::vector<LayerState> layers;
 };
 
@@ -193,8 +197,9 @@ rtv_status rtv_cache_create(const rtv_config* cfg, void* dev_buf, size_t bytes, 
   c->plan = p;
   c->base = static_cast<uint8_t*>(dev_buf);
   c->rope = reinterpret_cast<float*>(c->base);
+  c->ws = reinterpret_cast<float*>(c->base + p.rope_bytes);
   c->layers.resize(cfg->n_layers);
-  uint8_t* cur = c->base + p.rope_bytes;
+  uint8_t* cur = c->base + p.rope_bytes + p.ws_bytes;
   for (auto& L : c->layers) {
     L.kc = cur; cur += p.codes_bytes;
     L.vc = cur; cur += p.codes_bytes;
@@ -215,6 +220,7 @@ rtv_status rtv_cache_create(const rtv_config* cfg, void* dev_buf, size_t bytes, 
                                 hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemsetAsync(c->base + p.rope_bytes, 0, p.total - p.rope_bytes, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = rtv::attend_capacity(&c->capacity);
   if (e != hipSuccess) {
     delete c;
     return RTV_ERR_HIP;
@@ -341,6 +347,9 @@ rtv_status rtv_attend(rtv_cache* c, int32_t layer, const void* q_bf16, int64_t q
   const int qpb = rtv::attend_queries_per_block();
   a.n_qtiles = (n_tokens + qpb - 1) / qpb;
   a.n_work = a.n_qtiles * cfg.n_q_heads;
+  a.capacity = c->capacity;
+  a.ws_o = c->ws;
+  a.ws_ml = c->ws + (size_t)rtv::attend_max_parts() * qpb * cfg.head_dim;
   if (rtv::launch_attend(a, cfg.head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
     return RTV_ERR_HIP;
   return RTV_OK;
