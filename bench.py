@@ -31,11 +31,14 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak, TFLOP/s
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=4)
     p.add_argument("--layers", type=int, default=60)
     p.add_argument("--calls", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="after the timed steps, copy MIB MiB device-to-device once (a kernel of "
+                        "known traffic to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="HBM bytes per launch from rocprofv3 counters (optional)")
     return p.parse_args()
@@ -78,16 +81,17 @@ def cpu_baseline(wl):
         rng.standard_normal((C * T, wl.head_dim)).astype(np.float32)))
     vd = quant.dequantize_rows(*quant.quantize_rows(
         rng.standard_normal((C * T, wl.head_dim)).astype(np.float32)))
-    qr = rope.apply_rope(bf16.to_f32(q[:128, :1]), c[:128], s[:128])[:, 0]
+    rows = 256
+    qr = rope.apply_rope(bf16.to_f32(q[:rows, :1]), c[:rows], s[:rows])[:, 0]
     t0 = time.perf_counter()
     attention.attend_rows(qr, kd, vd)
     t_rows = time.perf_counter() - t0
-    t_attend = t_rows * (wl.chunk_tokens * wl.n_q_heads / 128)
+    t_attend = t_rows * (wl.chunk_tokens * wl.n_q_heads / rows)
     step_ms = (t_append + t_attend) * wl.n_layers * wl.calls_per_layer * 1e3
     return {
         "value": round(step_ms, 1), "unit": "ms/step", "cores": int(blas_threads), "kind": "oracle",
         "sample": (f"oracle RoPE+e4m3 upkeep of one frame ({T} tokens x {wl.n_kv_heads} heads) x {F}, "
-                   f"and float64 attention of 128 query rows of one head over {C * T} keys, "
+                   f"and float64 attention of {rows} query rows of one head over {C * T} keys, "
                    f"scaled to {wl.chunk_tokens}x{wl.n_q_heads} rows and "
                    f"{wl.n_layers * wl.calls_per_layer} calls per step"),
     }
@@ -213,6 +217,14 @@ def main():
         },
         "wall_s_timed": round(wall, 3),
     }
+    if args.copy_calibration:
+        nb = args.copy_calibration << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = nb
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

@@ -11,7 +11,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librtv.so")
+# RTV_LIB may name another build of the same library (e.g. a profiling build)
+LIB_PATH = os.environ.get("RTV_LIB") or os.path.join(_HERE, "librtv.so")
 
 RTV_OK = 0
 RTV_ERR_INVALID_ARG = -1

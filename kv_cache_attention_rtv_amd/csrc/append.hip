@@ -53,11 +53,43 @@ __device__ __forceinline__ int vt_key_of_pos4(int p4) {
   return 32 * (b >> 4) + 8 * ((b >> 2) & 3) + 4 * h;
 }
 
+// bf16 pieces of one lane: E elements at d0 and E at D/2 + d0
+template <int E>
+struct RowPiece {
+  uint32_t w0[E / 2], w1[E / 2];
+};
+
+template <int D>
+__device__ __forceinline__ RowPiece<D / 16> load_piece(const uint16_t* row, int g, bool valid) {
+  constexpr int E = D / 16;
+  RowPiece<E> r;
+  if constexpr (E == 8) {
+    uint4 p0 = make_uint4(0, 0, 0, 0), p1 = p0;
+    if (valid) {
+      p0 = *(const uint4*)(row + g * E);
+      p1 = *(const uint4*)(row + D / 2 + g * E);
+    }
+    r.w0[0] = p0.x; r.w0[1] = p0.y; r.w0[2] = p0.z; r.w0[3] = p0.w;
+    r.w1[0] = p1.x; r.w1[1] = p1.y; r.w1[2] = p1.z; r.w1[3] = p1.w;
+  } else {
+    uint2 p0 = make_uint2(0, 0), p1 = p0;
+    if (valid) {
+      p0 = *(const uint2*)(row + g * E);
+      p1 = *(const uint2*)(row + D / 2 + g * E);
+    }
+    r.w0[0] = p0.x; r.w0[1] = p0.y;
+    r.w1[0] = p1.x; r.w1[1] = p1.y;
+  }
+  return r;
+}
+
 template <int D>
 __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(AppendArgs a) {
   constexpr int E = D / 16;          // elements per lane per half
   constexpr int HALF = D / 2;
   constexpr int LDS_STRIDE = D + 4;  // bytes per V row in LDS
+  constexpr int ROWS = kAppendThreads / 8;           // rows per pass
+  constexpr int PASSES = kTileKeys / ROWS;
   __shared__ uint32_t vrow[kTileKeys * LDS_STRIDE / 4];
 
   const int u = xcd_remap(blockIdx.x, a.n_work);
@@ -72,54 +104,45 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
   const int tid = threadIdx.x;
   const int g = tid & 7;
 
-  for (int pass = 0; pass < kTileKeys / (kAppendThreads / 8); ++pass) {
-    const int r = pass * (kAppendThreads / 8) + (tid >> 3);   // key row within the tile
-    const int64_t slot = tile_lo + r;
-    const bool valid = slot >= lo && slot < hi;
-    const int64_t t = valid ? slot - a.write_slot : 0;         // token within the chunk
+  // ---- issue every global load of both passes before any arithmetic -------
+  RowPiece<E> kp[PASSES], vp[PASSES];
+  float4 cs[PASSES][E / 2];
+  bool valid[PASSES];
+  int64_t slot[PASSES];
+#pragma unroll
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int r = pass * ROWS + (tid >> 3);          // key row within the tile
+    slot[pass] = tile_lo + r;
+    valid[pass] = slot[pass] >= lo && slot[pass] < hi;
+    const int64_t t = valid[pass] ? slot[pass] - a.write_slot : 0;   // token in the chunk
+    kp[pass] = load_piece<D>(a.k + t * a.ldk + (int64_t)h * D, g, valid[pass]);
+    vp[pass] = load_piece<D>(a.v + t * a.ldv + (int64_t)h * D, g, valid[pass]);
+    const float4* tab = (const float4*)(a.rope + (t * HALF + g * E) * 2);
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) cs[pass][i] = valid[pass] ? tab[i] : make_float4(1.f, 0.f, 1.f, 0.f);
+  }
 
-    // ---- K: load, rotate, quantize, store ------------------------------
-    float x0[E], x1[E];
-    {
-      const uint16_t* src = a.k + t * a.ldk + (int64_t)h * D;
-      if constexpr (E == 8) {
-        uint4 p0 = valid ? *(const uint4*)(src + g * E) : make_uint4(0, 0, 0, 0);
-        uint4 p1 = valid ? *(const uint4*)(src + HALF + g * E) : make_uint4(0, 0, 0, 0);
-        const uint32_t w0[4] = {p0.x, p0.y, p0.z, p0.w};
-        const uint32_t w1[4] = {p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x0[2 * i] = bf16_lo(w0[i]); x0[2 * i + 1] = bf16_hi(w0[i]);
-          x1[2 * i] = bf16_lo(w1[i]); x1[2 * i + 1] = bf16_hi(w1[i]);
-        }
-      } else {
-        uint2 p0 = valid ? *(const uint2*)(src + g * E) : make_uint2(0, 0);
-        uint2 p1 = valid ? *(const uint2*)(src + HALF + g * E) : make_uint2(0, 0);
-        const uint32_t w0[2] = {p0.x, p0.y};
-        const uint32_t w1[2] = {p1.x, p1.y};
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          x0[2 * i] = bf16_lo(w0[i]); x0[2 * i + 1] = bf16_hi(w0[i]);
-          x1[2 * i] = bf16_lo(w1[i]); x1[2 * i + 1] = bf16_hi(w1[i]);
-        }
-      }
-    }
-    float r0[E], r1[E];
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int r = pass * ROWS + (tid >> 3);
+    // ---- K: rotate, quantize, store ------------------------------------
     {
-      const float4* cs = (const float4*)(a.rope + (t * HALF + g * E) * 2);
+      float r0[E], r1[E];
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < E / 2; ++i) {
-        const float4 c = valid ? cs[i] : make_float4(1.f, 0.f, 1.f, 0.f);  // (cos, sin) x 2
+        const float4 c = cs[pass][i];                 // (cos, sin) of two pairs
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+          const int e = 2 * i + j;
           const float co = j ? c.z : c.x;
           const float si = j ? c.w : c.y;
-          const int e = 2 * i + j;
-          const float a0 = x0[e] * co;
-          const float b0 = x1[e] * si;
-          const float a1 = x1[e] * co;
-          const float b1 = x0[e] * si;
+          const float x0 = (e & 1) ? bf16_hi(kp[pass].w0[e >> 1]) : bf16_lo(kp[pass].w0[e >> 1]);
+          const float x1 = (e & 1) ? bf16_hi(kp[pass].w1[e >> 1]) : bf16_lo(kp[pass].w1[e >> 1]);
+          const float a0 = x0 * co;
+          const float b0 = x1 * si;
+          const float a1 = x1 * co;
+          const float b1 = x0 * si;
           r0[e] = a0 - b0;
           r1[e] = a1 + b1;
           amax = fmaxf(amax, fmaxf(fabsf(r0[e]), fabsf(r1[e])));
@@ -127,8 +150,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
       }
       amax = dpp_max8(amax);
       const RowQuant q = row_quant(amax);
-      if (valid) {
-        uint8_t* dst = a.kc + ((int64_t)h * a.slots_padded + slot) * D;
+      if (valid[pass]) {
+        uint8_t* dst = a.kc + ((int64_t)h * a.slots_padded + slot[pass]) * D;
         if constexpr (E == 8) {
           uint2 c0, c1;
           c0.x = quant4(r0[0], r0[1], r0[2], r0[3], q);
@@ -141,33 +164,16 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
           *(uint32_t*)(dst + g * E) = quant4(r0[0], r0[1], r0[2], r0[3], q);
           *(uint32_t*)(dst + HALF + g * E) = quant4(r1[0], r1[1], r1[2], r1[3], q);
         }
-        if (g == 0) a.ks[(int64_t)h * a.slots_padded + slot] = q.s;
+        if (g == 0) a.ks[(int64_t)h * a.slots_padded + slot[pass]] = q.s;
       }
     }
-
-    // ---- V: load, quantize, stage row-major in LDS ----------------------
+    // ---- V: quantize, stage row-major in LDS ----------------------------
     {
-      const uint16_t* src = a.v + t * a.ldv + (int64_t)h * D;
-      if constexpr (E == 8) {
-        uint4 p0 = valid ? *(const uint4*)(src + g * E) : make_uint4(0, 0, 0, 0);
-        uint4 p1 = valid ? *(const uint4*)(src + HALF + g * E) : make_uint4(0, 0, 0, 0);
-        const uint32_t w0[4] = {p0.x, p0.y, p0.z, p0.w};
-        const uint32_t w1[4] = {p1.x, p1.y, p1.z, p1.w};
+      float x0[E], x1[E];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x0[2 * i] = bf16_lo(w0[i]); x0[2 * i + 1] = bf16_hi(w0[i]);
-          x1[2 * i] = bf16_lo(w1[i]); x1[2 * i + 1] = bf16_hi(w1[i]);
-        }
-      } else {
-        uint2 p0 = valid ? *(const uint2*)(src + g * E) : make_uint2(0, 0);
-        uint2 p1 = valid ? *(const uint2*)(src + HALF + g * E) : make_uint2(0, 0);
-        const uint32_t w0[2] = {p0.x, p0.y};
-        const uint32_t w1[2] = {p1.x, p1.y};
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          x0[2 * i] = bf16_lo(w0[i]); x0[2 * i + 1] = bf16_hi(w0[i]);
-          x1[2 * i] = bf16_lo(w1[i]); x1[2 * i + 1] = bf16_hi(w1[i]);
-        }
+      for (int e = 0; e < E; ++e) {
+        x0[e] = (e & 1) ? bf16_hi(vp[pass].w0[e >> 1]) : bf16_lo(vp[pass].w0[e >> 1]);
+        x1[e] = (e & 1) ? bf16_hi(vp[pass].w1[e >> 1]) : bf16_lo(vp[pass].w1[e >> 1]);
       }
       float amax = 0.0f;
 #pragma unroll
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
         row[(g * E) / 4 + i] = quant4(x0[4 * i], x0[4 * i + 1], x0[4 * i + 2], x0[4 * i + 3], q);
         row[(HALF + g * E) / 4 + i] = quant4(x1[4 * i], x1[4 * i + 1], x1[4 * i + 2], x1[4 * i + 3], q);
       }
-      if (valid && g == 0) a.vs[(int64_t)h * a.slots_padded + slot] = q.s;
+      if (valid[pass] && g == 0) a.vs[(int64_t)h * a.slots_padded + slot[pass]] = q.s;
     }
   }
   __syncthreads();

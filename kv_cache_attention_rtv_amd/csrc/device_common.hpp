@@ -77,13 +77,14 @@ __device__ __forceinline__ uint32_t sign_bytes4(float a, float b, float c, float
 }
 
 // Quantize four values of a row to four codes in one dword (byte k <- x_k).
+// Branch-free: for an all-zero row (s == 0) the quotient is garbage and the
+// select keeps only the signed zeros.
 __device__ __forceinline__ uint32_t quant4(float x0, float x1, float x2, float x3,
                                            const RowQuant& q) {
-  uint32_t signs = sign_bytes4(x0, x1, x2, x3);
-  if (q.s == 0.0f) return signs;            // all-zero row: signed zeros
+  const uint32_t signs = sign_bytes4(x0, x1, x2, x3);
   uint32_t w = cvt_fp8x2<false>(quant_mag(x0, q), quant_mag(x1, q), 0u);
   w = cvt_fp8x2<true>(quant_mag(x2, q), quant_mag(x3, q), w);
-  return w | signs;
+  return q.s == 0.0f ? signs : (w | signs);
 }
 
 // ---- XCD-aware block order ------------------------------------------------
