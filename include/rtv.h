@@ -61,6 +61,14 @@ typedef struct rtv_config {
   int32_t chunk_frames;      /* F: frames appended per call (4 on the pages) */
   int32_t capacity_frames;   /* C: ring capacity in frames; multiple of F */
   int32_t max_global_frames; /* frames the session may ever append: extent of the RoPE table */
+  int32_t query_terms;       /* e4m3 terms carrying each query through the matrix cores:
+                              * 1 (or 0): one term, relative rounding error 2^-4;
+                              * 2: hi + 2^-4 lo, relative error about 2^-8, for keys with
+                              * outlier channels or heavy tails, whose scores spread over
+                              * many binades and magnify the query's rounding (costs about
+                              * 20% more attention time on long windows).  Windows shorter
+                              * than 8192 keys always use two terms for queries and
+                              * probabilities. */
   double rope_base;          /* RoPE base (10000) */
 } rtv_config;
 

@@ -59,7 +59,7 @@ __device__ __forceinline__ v16f mfma_fp8_bscaled(const v8i& a, const v8i& b, con
 // two-term e4m3 of two values: hi = e4m3(x), lo = e4m3((x - hi) * 2^kLoShift)
 // (|x - hi| <= 2^-4 |x|, so the scaled residual stays in range)
 constexpr int kLoShift = 4;
-// windows shorter than this many keys use the two-term (PRECISE) kernel
+// windows shorter than this many keys also carry P' as two terms (PLO)
 constexpr int64_t kPreciseKeys = 8192;
 template <bool HIGH>
 __device__ __forceinline__ void split_fp8x2(float a, float b, uint32_t& hi, uint32_t& lo) {
@@ -260,12 +260,15 @@ __device__ __forceinline__ v8i softmax_tile(const v16f (&s)[2], const float* kf,
 // MASK = false: every segment boundary of the window falls on a 64-slot tile
 // boundary (the host checks), so no tile needs masking and the kernel carries
 // no masking code.  MASK = true handles any boundary.
-// PRECISE = true (short windows): Q and P' are carried as two e4m3 terms,
-// hi + 2^-kLoShift * lo, each product taking a second MFMA whose B operand is
-// scaled by 2^-kLoShift; the relative error of Q and P' drops from 2^-4 to
-// about 2^-8.  The FP8 rounding error of attention shrinks with the square
-// root of the window length, so long windows keep one e4m3 term.
-template <int D, bool MASK, bool PRECISE>
+// QLO / PLO: Q / P' are carried as two e4m3 terms, hi + 2^-kLoShift * lo,
+// each product taking a second MFMA whose B operand is scaled by
+// 2^-kLoShift; the relative error of the operand drops from 2^-4 to about
+// 2^-8.  The rounding error of P' averages out over the keys (it shrinks with
+// the square root of the window length), so only short windows need PLO.  The
+// rounding error of Q moves every score of a row coherently and is amplified
+// by large K channels: short windows always carry QLO, longer ones when the
+// cache was created for two query terms (keys with outlier channels).
+template <int D, bool MASK, bool QLO, bool PLO>
 __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
   using SM = Smem<D>;
   constexpr int NSTEP = D / 64;             // MFMA k-steps for K.Q^T
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
         else v[e] = (b < 16) ? r0[b] : r1[b - 16];
       }
       uint32_t c = 0, lo = 0;
-      if constexpr (PRECISE) {
+      if constexpr (QLO) {
         split_fp8x2<false>(v[0], v[1], c, lo);
         split_fp8x2<true>(v[2], v[3], c, lo);
       } else {
@@ -484,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s) {
           acc_s[sub][kh] = mfma_fp8(kop[kh][s], qop[sub][s], acc_s[sub][kh]);
-          if constexpr (PRECISE)
+          if constexpr (QLO)
             acc_s[sub][kh] = mfma_fp8_bscaled(kop[kh][s], qlo[sub][s], acc_s[sub][kh], 127 - kLoShift);
         }
       }
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
     // softmax of sub-tile 0 (overlaps the sub-tile 1 MFMAs), then its PV with
     // the V operands that sub-tile 1 reuses
     v8i plo;
-    v8i pop = softmax_tile<NDT, PRECISE>(acc_s[0], kf, wf, hh, m_run[0], l_run[0], acc_o[0], plo);
+    v8i pop = softmax_tile<NDT, PLO>(acc_s[0], kf, wf, hh, m_run[0], l_run[0], acc_o[0], plo);
     v8i vop[NDT];
 #pragma unroll
     for (int d = 0; d < NDT; ++d) {
@@ -517,15 +520,15 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
       vop[d] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
                    (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
       acc_o[0][d] = mfma_fp8(vop[d], pop, acc_o[0][d]);
-      if constexpr (PRECISE) acc_o[0][d] = mfma_fp8_bscaled(vop[d], plo, acc_o[0][d], 127 - kLoShift);
+      if constexpr (PLO) acc_o[0][d] = mfma_fp8_bscaled(vop[d], plo, acc_o[0][d], 127 - kLoShift);
     }
 #pragma unroll
     for (int sub = 1; sub < kSub; ++sub) {
-      pop = softmax_tile<NDT, PRECISE>(acc_s[sub], kf, wf, hh, m_run[sub], l_run[sub], acc_o[sub], plo);
+      pop = softmax_tile<NDT, PLO>(acc_s[sub], kf, wf, hh, m_run[sub], l_run[sub], acc_o[sub], plo);
 #pragma unroll
       for (int d = 0; d < NDT; ++d) {
         acc_o[sub][d] = mfma_fp8(vop[d], pop, acc_o[sub][d]);
-        if constexpr (PRECISE) acc_o[sub][d] = mfma_fp8_bscaled(vop[d], plo, acc_o[sub][d], 127 - kLoShift);
+        if constexpr (PLO) acc_o[sub][d] = mfma_fp8_bscaled(vop[d], plo, acc_o[sub][d], 127 - kLoShift);
       }
     }
 
@@ -636,7 +639,7 @@ hipError_t attend_capacity(int* workgroups) {
   hipDeviceProp_t prop;
   if (e == hipSuccess) e = hipGetDeviceProperties(&prop, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_kernel<128, false, false>, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_kernel<128, false, false, false>, kThreads, 0);
   if (e != hipSuccess) return e;
   *workgroups = (per_cu > 0 ? per_cu : 1) * prop.multiProcessorCount;
   return hipSuccess;
@@ -653,7 +656,8 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
     if (args.seg_hi[s] > args.seg_lo[s])
       n_tiles += (int)((args.seg_hi[s] - 1) / 64 - args.seg_lo[s] / 64 + 1);
   }
-  const bool precise = keys < kPreciseKeys;
+  const bool short_window = keys < kPreciseKeys;
+  const bool two_term_q = short_window || args.two_term_q;
 
   // Schedule: whole rounds of the device's concurrent workgroups run whole
   // windows; the remainder, which would leave most of the device idle in a
@@ -671,21 +675,25 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
   args.full_per_xcd = (args.n_full + 7) / 8;
   args.parts_per_xcd = (args.n_parts + 7) / 8;
   const dim3 g(8 * (args.full_per_xcd + args.parts_per_xcd)), b(kThreads);
-#define RTV_LAUNCH(DIM, MASK, PREC) \
-  hipLaunchKernelGGL((attend_kernel<DIM, MASK, PREC>), g, b, 0, stream, args)
-  if (head_dim == 128) {
-    if (precise) {
-      if (aligned) RTV_LAUNCH(128, false, true); else RTV_LAUNCH(128, true, true);
-    } else {
-      if (aligned) RTV_LAUNCH(128, false, false); else RTV_LAUNCH(128, true, false);
-    }
-  } else {
-    if (precise) {
-      if (aligned) RTV_LAUNCH(64, false, true); else RTV_LAUNCH(64, true, true);
-    } else {
-      if (aligned) RTV_LAUNCH(64, false, false); else RTV_LAUNCH(64, true, false);
-    }
+#define RTV_LAUNCH(DIM, MASK, QL, PL) \
+  hipLaunchKernelGGL((attend_kernel<DIM, MASK, QL, PL>), g, b, 0, stream, args)
+#define RTV_DISPATCH_MASK(DIM, QL, PL) \
+  if (aligned) RTV_LAUNCH(DIM, false, QL, PL); else RTV_LAUNCH(DIM, true, QL, PL);
+#define RTV_DISPATCH(DIM)                                 \
+  if (short_window) {                                     \
+    RTV_DISPATCH_MASK(DIM, true, true)                    \
+  } else if (two_term_q) {                                \
+    RTV_DISPATCH_MASK(DIM, true, false)                   \
+  } else {                                                \
+    RTV_DISPATCH_MASK(DIM, false, false)                  \
   }
+  if (head_dim == 128) {
+    RTV_DISPATCH(128)
+  } else {
+    RTV_DISPATCH(64)
+  }
+#undef RTV_DISPATCH
+#undef RTV_DISPATCH_MASK
 #undef RTV_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || rem == 0) return e;

@@ -1,0 +1,294 @@
+// Projection step of the largest workload: per-tensor e4m3 quantization and an
+// FP8 GEMM on the gfx950 matrix cores.
+//
+// The pages name a fused FP8 matmul in the serving step (page "Runway explains
+// how it serves a 57B video model in real time", fourth paragraph) without a
+// formula; the reading implemented here is one scale per tensor,
+//   s = RN(amax / 448),  code = e4m3(RN(x / s))  (the cache's row rule with the
+//   whole tensor as the row),
+//   C = bf16( (s_a * s_b) * sum_k dec(A[m,k]) * dec(B[k,n]) ), f32 accumulation.
+//
+// GEMM decomposition: one workgroup = a 256 x 256 tile of C, 8 waves in a
+// 2 (M) x 4 (N) grid, each wave 128 x 64 = 4 x 2 blocks of
+// v_mfma_f32_32x32x64_f8f6f4.  The Bt block is the MFMA A operand and the A
+// block the B operand, so a lane of the result holds four consecutive output
+// columns of one row (one 8-byte bf16 store).  K advances 128 bytes per stage
+// through two LDS stages (rows padded to 144 B, conflict-free 16-byte reads);
+// the global loads of stage t+1 are in flight while stage t is computed.
+// Tiles are numbered XCD-aware (each XCD walks a contiguous range) and grouped
+// four M-rows at a time so the workgroups resident on one XCD share operands
+// in its L2.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+
+namespace rtv {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kGemmWaves = 8;
+constexpr int kGemmThreads = kGemmWaves * kWave;
+constexpr int kRow = kBK + 16;                       // padded LDS row (bytes)
+constexpr int kStageBytes = (kBM + kBN) * kRow;      // 73728
+constexpr int kGroupM = 4;
+constexpr int kChunksPerThread = (kBM + kBN) * (kBK / 16) / kGemmThreads;  // 8
+
+constexpr int kQuantThreads = 256;
+
+__device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// ---- per-tensor quantization ------------------------------------------------
+
+// largest |x| over bf16 values, as bits: for non-NaN bf16 the order of
+// (bits & 0x7FFF) is the order of |x|
+__device__ __forceinline__ uint32_t mag_max8(uint4 w) {
+  uint32_t m = 0;
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = max(m, ws[i] & 0x7FFFu);
+    m = max(m, (ws[i] >> 16) & 0x7FFFu);
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = m;
+  __syncthreads();
+  m = 0;
+#pragma unroll
+  for (int i = 0; i < kQuantThreads / kWave; ++i) m = max(m, red[i]);
+  return m;
+}
+
+__global__ void __launch_bounds__(kQuantThreads)
+quant_amax_kernel(const uint16_t* __restrict__ x, int64_t n, uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[kQuantThreads / kWave];
+  const int64_t n8 = n >> 3;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n8; i += stride)
+    m = max(m, mag_max8(xv[i]));
+  if (blockIdx.x == 0)
+    for (int64_t i = (n8 << 3) + threadIdx.x; i < n; i += kQuantThreads) m = max(m, x[i] & 0x7FFFu);
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+__device__ __forceinline__ uint32_t quant_one(float x, const RowQuant& q) {
+  const uint32_t sign = (__float_as_uint(x) >> 31) << 7;
+  if (q.s == 0.0f) return sign;
+  return (cvt_fp8x2<false>(quant_mag(x, q), 0.0f, 0u) & 0xFFu) | sign;
+}
+
+__global__ void __launch_bounds__(kQuantThreads)
+quant_apply_kernel(const uint16_t* __restrict__ x, int64_t n, const uint32_t* __restrict__ partial,
+                   int n_partial, uint8_t* __restrict__ codes, float* __restrict__ scale) {
+  __shared__ uint32_t red[kQuantThreads / kWave];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n_partial; i += kQuantThreads) m = max(m, partial[i]);
+  m = block_max(m, red);
+  const RowQuant q = row_quant(__uint_as_float(m << 16));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = q.s;
+  const int64_t n8 = n >> 3;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint2* cv = reinterpret_cast<uint2*>(codes);
+  const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n8; i += stride) {
+    const uint4 w = xv[i];
+    uint2 o;
+    o.x = quant4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), q);
+    o.y = quant4(bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w), q);
+    cv[i] = o;
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = (n8 << 3) + threadIdx.x; i < n; i += kQuantThreads)
+      codes[i] = (uint8_t)quant_one(__uint_as_float((uint32_t)x[i] << 16), q);
+}
+
+// ---- GEMM -------------------------------------------------------------------
+
+struct GemmArgs {
+  const uint8_t* a;    // [M][K]
+  const uint8_t* bt;   // [N][K]
+  const float* sa;
+  const float* sb;
+  uint16_t* c;         // [M][ldc] bf16
+  int64_t ldc;
+  int32_t M, N, K;
+  int32_t n_mt, n_nt, n_tiles;
+  int32_t vec_store;   // 8-byte stores allowed (c 8-aligned, ldc % 4 == 0)
+};
+
+// global -> register loads of one stage: chunk c of 16 bytes, rows [0, 256)
+// of A then of Bt, 8 chunks per row; rows past M / N repeat the last row and
+// k past K reads zeros
+struct StageRegs {
+  uint4 r[kChunksPerThread];
+};
+
+__device__ __forceinline__ void load_stage(StageRegs& s, const GemmArgs& g, int m0, int n0, int k0) {
+#pragma unroll
+  for (int j = 0; j < kChunksPerThread; ++j) {
+    const int c = threadIdx.x + j * kGemmThreads;
+    const int row = c >> 3;                 // 0..511
+    const int col = (c & 7) * 16;
+    const bool is_a = row < kBM;
+    const int r = is_a ? min(m0 + row, g.M - 1) : min(n0 + row - kBM, g.N - 1);
+    const uint8_t* base = is_a ? g.a : g.bt;
+    if (k0 + col < g.K)
+      s.r[j] = *reinterpret_cast<const uint4*>(base + (int64_t)r * g.K + k0 + col);
+    else
+      s.r[j] = make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void store_stage(const StageRegs& s, uint8_t* st) {
+#pragma unroll
+  for (int j = 0; j < kChunksPerThread; ++j) {
+    const int c = threadIdx.x + j * kGemmThreads;
+    *reinterpret_cast<uint4*>(st + (c >> 3) * kRow + (c & 7) * 16) = s.r[j];
+  }
+}
+
+// 32-row operand fragment at k-substep ks: lane (i, hh) reads row i, bytes
+// [64 ks + 32 hh, +32) (A and B use the same byte-to-k assignment)
+__device__ __forceinline__ v8i frag(const uint8_t* st, int row0, int ks, int lane) {
+  const uint8_t* p = st + (row0 + (lane & 31)) * kRow + ks * 64 + (lane >> 5) * 32;
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
+  v8i v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+__global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int logical = xcd_remap(blockIdx.x, g.n_tiles);
+  if (logical < 0) return;
+  // group kGroupM tile rows: consecutive logical tiles walk down a column of
+  // the group first
+  const int group_size = kGroupM * g.n_nt;
+  const int grp = logical / group_size;
+  const int first_m = grp * kGroupM;
+  const int gm = min(g.n_mt - first_m, kGroupM);
+  const int in_grp = logical - grp * group_size;
+  const int mt = first_m + in_grp % gm;
+  const int nt = in_grp / gm;
+  const int m0 = mt * kBM, n0 = nt * kBN;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int wm = (wave & 1) * 128;      // wave's M offset in the tile
+  const int wn = (wave >> 1) * 64;      // wave's N offset in the tile
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int n_k = (g.K + kBK - 1) / kBK;
+  StageRegs regs;
+  load_stage(regs, g, m0, n0, 0);
+  store_stage(regs, smem);
+  __syncthreads();
+  for (int t = 0; t < n_k; ++t) {
+    const bool more = t + 1 < n_k;
+    if (more) load_stage(regs, g, m0, n0, (t + 1) * kBK);
+    const uint8_t* st = smem + (t & 1) * kStageBytes;
+    const uint8_t* sa = st;                 // A rows
+    const uint8_t* sbt = st + kBM * kRow;   // Bt rows
+#pragma unroll
+    for (int ks = 0; ks < kBK / 64; ++ks) {
+      v8i bop[2], aop[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bop[j] = frag(sbt, wn + 32 * j, ks, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) aop[i] = frag(sa, wm + 32 * i, ks, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_fp8(bop[j], aop[i], acc[i][j]);
+    }
+    if (more) store_stage(regs, smem + ((t + 1) & 1) * kStageBytes);
+    __syncthreads();
+  }
+
+  // epilogue: acc[i][j] holds D[n][m] for m = m0+wm+32i + lane%32 and
+  // n = n0+wn+32j + 8(r/4) + 4(lane/32) + r%4
+  const float s = (*g.sa) * (*g.sb);
+  const int hh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm + 32 * i + (lane & 31);
+    if (m >= g.M) continue;
+    uint16_t* crow = g.c + (int64_t)m * g.ldc;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int grp4 = 0; grp4 < 4; ++grp4) {
+        const int n = n0 + wn + 32 * j + 8 * grp4 + 4 * hh;
+        const float v0 = acc[i][j][4 * grp4 + 0] * s, v1 = acc[i][j][4 * grp4 + 1] * s;
+        const float v2 = acc[i][j][4 * grp4 + 2] * s, v3 = acc[i][j][4 * grp4 + 3] * s;
+        if (g.vec_store && n + 4 <= g.N) {
+          uint2 o;
+          o.x = pack_bf16x2(v0, v1);
+          o.y = pack_bf16x2(v2, v3);
+          *reinterpret_cast<uint2*>(crow + n) = o;
+        } else {
+          const float vs[4] = {v0, v1, v2, v3};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < g.N) crow[n + e] = (uint16_t)f32_to_bf16_bits(vs[e]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int quant_max_partials() { return 1024; }
+
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, uint8_t* codes, float* scale,
+                            uint32_t* partial, hipStream_t stream) {
+  const int64_t per_block = (int64_t)kQuantThreads * 8 * 4;
+  const int blocks = (int)std::min<int64_t>(quant_max_partials(), std::max<int64_t>(1, (n + per_block - 1) / per_block));
+  hipLaunchKernelGGL(quant_amax_kernel, dim3(blocks), dim3(kQuantThreads), 0, stream, x, n, partial);
+  hipLaunchKernelGGL(quant_apply_kernel, dim3(blocks), dim3(kQuantThreads), 0, stream, x, n,
+                     (const uint32_t*)partial, blocks, codes, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const uint8_t* a, const float* sa, const uint8_t* bt, const float* sb,
+                           uint16_t* c, int M, int N, int K, int64_t ldc, hipStream_t stream) {
+  const hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
+  if (e != hipSuccess) return e;
+  GemmArgs g;
+  g.a = a; g.bt = bt; g.sa = sa; g.sb = sb; g.c = c; g.ldc = ldc;
+  g.M = M; g.N = N; g.K = K;
+  g.n_mt = (M + kBM - 1) / kBM;
+  g.n_nt = (N + kBN - 1) / kBN;
+  g.n_tiles = g.n_mt * g.n_nt;
+  g.vec_store = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
+  const int grid = (g.n_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL(gemm_fp8_kernel, dim3(grid), dim3(kGemmThreads), 2 * kStageBytes, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace rtv

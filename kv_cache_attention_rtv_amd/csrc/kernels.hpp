@@ -42,6 +42,7 @@ struct AttendArgs {
   int32_t n_qtiles;       // ceil(n_tokens / queries per workgroup)
   int32_t n_work;         // n_qtiles * n_q_heads (units of work)
   int32_t capacity;       // workgroups the device runs concurrently (0 = never split)
+  int32_t two_term_q;     // queries as two e4m3 terms on every window
   // schedule (filled by launch_attend): units [0, n_full) run whole windows; units [n_full, n_work) are
   // split into parts_per_unit key ranges whose partial (O, m, l) go to the
   // workspace and are merged by the combine kernel
@@ -63,5 +64,12 @@ hipError_t launch_append(const AppendArgs& args, int head_dim, hipStream_t strea
 hipError_t launch_attend(const AttendArgs& args, int head_dim, hipStream_t stream);
 hipError_t launch_encode_e4m3(const float* x, uint8_t* out, int64_t n, hipStream_t stream);
 int attend_queries_per_block();
+
+// per-tensor e4m3 quantization (partial: quant_max_partials() u32 of workspace)
+int quant_max_partials();
+hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, uint8_t* codes, float* scale,
+                            uint32_t* partial, hipStream_t stream);
+hipError_t launch_gemm_fp8(const uint8_t* a, const float* sa, const uint8_t* bt, const float* sb,
+                           uint16_t* c, int M, int N, int K, int64_t ldc, hipStream_t stream);
 
 }  // namespace rtv

@@ -58,6 +58,7 @@ rtv_status check_config(const rtv_config* c) {
   if (c->capacity_frames < c->chunk_frames || c->capacity_frames % c->chunk_frames) return RTV_ERR_INVALID_ARG;
   if (c->max_global_frames < c->chunk_frames) return RTV_ERR_INVALID_ARG;
   if (!(c->rope_base > 0.0) || !std::isfinite(c->rope_base)) return RTV_ERR_INVALID_ARG;
+  if (c->query_terms < 0 || c->query_terms > 2) return RTV_ERR_INVALID_ARG;
   int64_t chunk;
   if (!mul_ok(c->chunk_frames, c->tokens_per_frame, &chunk) || chunk > INT32_MAX) return RTV_ERR_INVALID_ARG;
   return RTV_OK;
@@ -348,6 +349,7 @@ rtv_status rtv_attend(rtv_cache* c, int32_t layer, const void* q_bf16, int64_t q
   a.n_qtiles = (n_tokens + qpb - 1) / qpb;
   a.n_work = a.n_qtiles * cfg.n_q_heads;
   a.capacity = c->capacity;
+  a.two_term_q = cfg.query_terms == 2;
   a.ws_o = c->ws;
   a.ws_ml = c->ws + (size_t)rtv::attend_max_parts() * qpb * cfg.head_dim;
   if (rtv::launch_attend(a, cfg.head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -376,6 +378,39 @@ rtv_status rtv_encode_e4m3(const float* x_dev, uint8_t* codes_dev, int64_t n, vo
   if (reinterpret_cast<uintptr_t>(x_dev) % 16 || reinterpret_cast<uintptr_t>(codes_dev) % 4)
     return RTV_ERR_INVALID_ARG;
   if (rtv::launch_encode_e4m3(x_dev, codes_dev, n, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return RTV_ERR_HIP;
+  return RTV_OK;
+}
+
+size_t rtv_quant_workspace_bytes(int64_t n) {
+  (void)n;
+  return sizeof(uint32_t) * (size_t)rtv::quant_max_partials();
+}
+
+rtv_status rtv_quant_fp8_per_tensor(const void* x_bf16, int64_t n, uint8_t* codes_dev,
+                                    float* scale_dev, void* workspace, void* stream) {
+  if (n < 0 || !scale_dev || !workspace || (n > 0 && (!x_bf16 || !codes_dev))) return RTV_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(x_bf16) % 16 || reinterpret_cast<uintptr_t>(codes_dev) % 8 ||
+      reinterpret_cast<uintptr_t>(scale_dev) % 4 || reinterpret_cast<uintptr_t>(workspace) % 4)
+    return RTV_ERR_INVALID_ARG;
+  if (rtv::launch_quant_fp8(static_cast<const uint16_t*>(x_bf16), n, codes_dev, scale_dev,
+                            static_cast<uint32_t*>(workspace), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return RTV_ERR_HIP;
+  return RTV_OK;
+}
+
+rtv_status rtv_gemm_fp8(const uint8_t* a, const float* sa_dev, const uint8_t* bt,
+                        const float* sb_dev, void* c_bf16, int32_t M, int32_t N, int32_t K,
+                        int64_t ldc, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || ldc < N) return RTV_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return RTV_OK;
+  if (!a || !bt || !sa_dev || !sb_dev || !c_bf16) return RTV_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(bt) % 16 ||
+      reinterpret_cast<uintptr_t>(c_bf16) % 2 || reinterpret_cast<uintptr_t>(sa_dev) % 4 ||
+      reinterpret_cast<uintptr_t>(sb_dev) % 4)
+    return RTV_ERR_INVALID_ARG;
+  if (rtv::launch_gemm_fp8(a, sa_dev, bt, sb_dev, static_cast<uint16_t*>(c_bf16), M, N, K, ldc,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
     return RTV_ERR_HIP;
   return RTV_OK;
 }

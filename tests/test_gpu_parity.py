@@ -22,14 +22,14 @@ MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
 
 
-def _caches(rtv, wl, max_global_frames=None, n_layers=None):
+def _caches(rtv, wl, max_global_frames=None, n_layers=None, query_terms=1):
     steps = max(wl.steps, 1)
     cfg = rtv.RtvConfig(
         n_layers=n_layers or wl.n_layers, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
         head_dim=wl.head_dim, tokens_per_frame=wl.tokens_per_frame, chunk_frames=wl.chunk_frames,
         capacity_frames=wl.capacity_frames,
         max_global_frames=max_global_frames or (steps + 2) * wl.chunk_frames,
-        rope_base=wl.rope_base)
+        rope_base=wl.rope_base, query_terms=query_terms)
     gpu = rtv.RtvCache(cfg)
     ora = OracleKVCache(cfg.n_layers, wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame,
                         wl.chunk_frames, wl.capacity_frames, wl.rope_base)
@@ -219,5 +219,52 @@ def test_unaligned_chunks(rtv_lib, T, F, C, D, H, Hq, steps):
             mx, mean = attention_errors(bf16_to_np_f32(out), want)
             assert mx <= MAX_ABS and mean <= MEAN_ABS, (step, maxw, mx, mean)
         _check_ring(gpu, ora, 0)
+        gpu.advance(0)
+        ora.advance(0)
+
+
+def test_stress_outliers_zero_rows_window_cycle(rtv_lib):
+    """Student-t (nu = 3) K/V with four x20 outlier channels per head and 1 %
+    all-zero token rows, a 24-frame ring and a window cycling over 4..24 frames.
+    Codes/scales bit-exact (zero rows: scale 0, codes 0x00); attention checked
+    normalised by the window's max |V| (heavy tails make absolute errors scale
+    with |V|).  The cache carries queries as two e4m3 terms: the outlier
+    channels spread the scores over many binades, where one term's rounding
+    (2^-4 relative) would move the heaviest keys' weights too far."""
+    from workloads.generate import zero_rows
+    wl = get_workload("stress")
+    gpu, ora = _caches(rtv_lib, wl, max_global_frames=10 * wl.chunk_frames, query_terms=2)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, wl.chunk_tokens - 1], rng.integers(0, wl.chunk_tokens, 30)]))
+    cycle = wl.window_cycle
+    worst = (0.0, 0.0)
+    for step in range(8):
+        q, k, v = qkv_normal(wl, 0, step, 0)
+        print(f"stress step={step}", flush=True)
+        gpu.append(0, to_dev_bf16(k), to_dev_bf16(v))
+        e = ora.append(0, k, v)
+        L = gpu.layout(0)
+        slots = L.head_frame * wl.tokens_per_frame + np.arange(wl.chunk_tokens)
+        gk, gks, gv, gvs = ring_rows(gpu, 0, slots)
+        assert np.array_equal(gk, e.k_codes) and np.array_equal(gv, e.v_codes)
+        assert np.array_equal(gks.view(np.uint32), e.k_scales.view(np.uint32))
+        assert np.array_equal(gvs.view(np.uint32), e.v_scales.view(np.uint32))
+        z = zero_rows(wl, 0, step, 0)
+        # zero rows: scale 0 and signed-zero codes (RoPE of a zero row may give -0)
+        assert np.all(gks[z] == 0) and np.all(gvs[z] == 0)
+        assert np.all((gk[z] & 0x7F) == 0) and np.all(gv[z] == 0)
+        maxw = cycle[(step + 3) % len(cycle)]
+        out = gpu.attend(0, to_dev_bf16(q), max_window_frames=maxw)
+        if step >= 4:
+            want = ora.attend(0, q, max_window_frames=maxw, rows=rows)
+            _, _, _, _, vc, vs = ora.window(0, maxw)
+            from oracle import quant
+            got = bf16_to_np_f32(out)[rows]
+            for h in range(wl.n_q_heads):
+                vmax = np.abs(quant.dequantize_rows(vc[:, h], vs[:, h])).max()
+                err = np.abs(got[:, h].astype(np.float64) - want[:, h]) / vmax
+                worst = (max(worst[0], err.max()), max(worst[1], err.mean()))
+                assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (step, maxw, h, err.max(), err.mean())
+            print(f"stress step={step} window={maxw} normalised worst so far max={worst[0]:.3e} mean={worst[1]:.3e}", flush=True)
         gpu.advance(0)
         ora.advance(0)

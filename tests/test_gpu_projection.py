@@ -1,0 +1,305 @@
+"""GPU parity of the projection workload: per-tensor e4m3 quantization
+(bit-exact), the FP8 GEMM (within its float32-accumulation bound), the append
+fed from the GEMM's strided K/V columns, and attention of 24 query heads over
+12 KV heads on a 32-frame ring.
+
+The GEMM result is not unique: float32 accumulation may round to the other
+bfloat16 neighbour where the exact value lies within the accumulation error of
+a rounding boundary.  The oracle's cache is therefore fed from the oracle's
+own GEMM; (token, head) rows whose bf16 input differs from the GPU's (at
+K = 6144 most 128-element rows hold at least one such element) are checked for
+validity (within one e4m3 step), every other row bit for bit.  The append from
+the projection's strided layout is checked bit for bit on its own, from K/V
+columns the oracle supplies.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bf16 as obf16
+from oracle import e4m3 as oe4m3
+from oracle import gemm as ogemm
+from oracle import quant as oquant
+from oracle import rope as orope
+from oracle.cache import OracleKVCache
+from tests.gpu_helpers import attention_errors, bf16_to_np_f32, ring_rows, to_dev_bf16
+from workloads import get_workload, query_normal, qkv_normal
+from workloads.generate import projection_inputs
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def _np_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _gemm_tolerance(a_codes, sa, b_codes, sb, exact):
+    """|gpu - exact| bound: the matrix core's error bound (float32 accumulation
+    and its in-group alignment), the rounding of sa*sb and of the scaling
+    product (2^-23 relative together), and half a bf16 ulp (2^-8 relative)."""
+    eb = ogemm.error_bound(a_codes, sa, b_codes, sb)
+    mag = np.abs(exact) + eb
+    return eb * (1 + 2.0 ** -20) + 2.0 ** -22 * mag + 2.0 ** -8 * mag
+
+
+def _check_gemm(got_bits, a_codes, sa, b_codes, sb, min_same=0.95):
+    """Every output within the bound, and most equal to the correctly rounded
+    exact value (a wrong k range or operand would make nearly all differ)."""
+    exact = ogemm.gemm_fp64(a_codes, sa, b_codes, sb)
+    got = obf16.to_f32(got_bits).astype(np.float64)
+    tol = _gemm_tolerance(a_codes, sa, b_codes, sb, exact)
+    bad = np.abs(got - exact) > tol
+    assert not bad.any(), f"{bad.sum()} GEMM outputs outside the bound, first at {np.argwhere(bad)[:3].tolist()}"
+    same = np.mean(got_bits == obf16.from_f64(exact))
+    print(f"  GEMM outputs equal to the correctly rounded value: {same:.4f}", flush=True)
+    assert same >= min_same, f"only {same:.4f} of the outputs equal the correctly rounded result"
+    return exact
+
+
+def _random_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E        # no NaN codes
+    return c
+
+
+@pytest.mark.parametrize("n,kind", [(1, "normal"), (7, "normal"), (8, "normal"), (1000, "normal"),
+                                    (4097 * 8 + 3, "normal"), (300001, "outlier"), (4099, "zero"),
+                                    (2051, "tiny")])
+def test_quant_per_tensor_matches_oracle(rtv_lib, n, kind):
+    rng = np.random.default_rng(n)
+    x = rng.standard_normal(n).astype(np.float32)
+    if kind == "outlier":
+        x[n // 3] = -3.0e4
+    elif kind == "zero":
+        x[:] = 0.0
+        x[::3] = -0.0
+    elif kind == "tiny":
+        x *= np.float32(1e-37)
+    bits = obf16.from_f64(x.astype(np.float64))
+    print(f"quant n={n} kind={kind}", flush=True)
+    codes, scale = rtv_lib.quant_fp8_per_tensor(to_dev_bf16(bits))
+    want_c, want_s = ogemm.quantize_per_tensor(obf16.to_f32(bits))
+    assert np.float32(scale.item()).view(np.uint32) == np.float32(want_s).view(np.uint32)
+    assert np.array_equal(codes.cpu().numpy(), want_c)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (300, 200, 192), (257, 513, 320), (64, 4608, 128),
+                                   (511, 260, 6144)])
+def test_gemm_ragged_shapes(rtv_lib, M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    a = _random_codes(rng, (M, K))
+    bt = _random_codes(rng, (N, K))
+    sa, sb = np.float32(0.0123), np.float32(3.7e-3)
+    print(f"gemm M={M} N={N} K={K}", flush=True)
+    dev = torch.device("cuda")
+    out = rtv_lib.gemm_fp8(torch.from_numpy(a).to(dev), torch.tensor([sa], dtype=torch.float32, device=dev),
+                           torch.from_numpy(bt).to(dev), torch.tensor([sb], dtype=torch.float32, device=dev))
+    _check_gemm(_np_bits(out), a, sa, bt.T, sb, min_same=0.9)
+
+
+def test_gemm_strided_output_and_errors(rtv_lib):
+    rng = np.random.default_rng(5)
+    M, N, K, ldc = 130, 70, 128, 77         # odd row stride: element stores
+    a, bt = _random_codes(rng, (M, K)), _random_codes(rng, (N, K))
+    dev = torch.device("cuda")
+    big = torch.full((M, ldc), 7, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    out = big[:, :N]
+    sa = torch.tensor([0.5], dtype=torch.float32, device=dev)
+    sb = torch.tensor([0.25], dtype=torch.float32, device=dev)
+    rtv_lib.gemm_fp8(torch.from_numpy(a).to(dev), sa, torch.from_numpy(bt).to(dev), sb, out=out)
+    _check_gemm(_np_bits(out.contiguous()), a, 0.5, bt.T, 0.25, min_same=0.9)
+    assert np.all(_np_bits(big)[:, N:] == 7), "GEMM wrote outside its columns"
+    abi = rtv_lib.abi
+    at, btt = torch.from_numpy(a).to(dev), torch.from_numpy(bt).to(dev)
+    for args in [(M, N, 100, ldc), (M, N, 0, ldc), (-1, N, K, ldc), (M, N, K, N - 1)]:
+        with pytest.raises(rtv_lib.RtvError) as e:
+            abi.rtv_gemm_fp8(at.data_ptr(), sa.data_ptr(), btt.data_ptr(), sb.data_ptr(),
+                             out.data_ptr(), *args, torch.cuda.current_stream().cuda_stream)
+        assert e.value.status == abi.RTV_ERR_INVALID_ARG
+
+
+def _proj_cache(rtv, wl, steps):
+    cfg = rtv.RtvConfig(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame,
+                        wl.chunk_frames, wl.capacity_frames, (steps + 1) * wl.chunk_frames, wl.rope_base)
+    return rtv.RtvCache(cfg)
+
+
+def _kv_views(out, wl):
+    """K and V of the projection output (columns [H*D, 2H*D) and [2H*D, 3H*D)),
+    [n, H, D] views with token stride proj_width."""
+    H, D = wl.n_kv_heads, wl.head_dim
+    k = out[:, H * D:2 * H * D].unflatten(1, (H, D))
+    v = out[:, 2 * H * D:3 * H * D].unflatten(1, (H, D))
+    return k, v
+
+
+def _check_rows_against_oracle(g_codes, g_scales, w_codes, w_scales, same_rows):
+    """Bit-exact where the (token, head) input row is the oracle's; elsewhere
+    the dequantized rows agree within one e4m3 step of the row's max."""
+    assert same_rows.any(), "no K/V input row equals the oracle's"
+    s = same_rows
+    assert np.array_equal(g_codes[s], w_codes[s])
+    assert np.array_equal(g_scales[s].view(np.uint32), w_scales[s].view(np.uint32))
+    d = ~s
+    if d.any():
+        gd = oquant.dequantize_rows(g_codes[d], g_scales[d])
+        wd = oquant.dequantize_rows(w_codes[d], w_scales[d])
+        amax = np.maximum(np.abs(wd).max(axis=-1, keepdims=True), 1e-30)
+        assert np.all(np.abs(gd - wd) <= 2.0 ** -3 * amax + 1e-30)
+
+
+def test_projection_full_size_sampled(rtv_lib):
+    """X [11968 x 6144] and W [6144 x 4608] at the workload's size: both
+    quantizations bit-exact in full, the GEMM on sampled rows, and the append
+    of the GEMM's strided K/V columns on the sampled tokens."""
+    wl = get_workload("proj")
+    dev = torch.device("cuda")
+    x, w = projection_inputs(wl, 0, 0)
+    print("proj full: quantize", flush=True)
+    xc, sx = rtv_lib.quant_fp8_per_tensor(to_dev_bf16(x))
+    wtc, sw = rtv_lib.quant_fp8_per_tensor(to_dev_bf16(np.ascontiguousarray(w.T)))
+    want_xc, want_sx = ogemm.quantize_per_tensor(obf16.to_f32(x))
+    want_wc, want_sw = ogemm.quantize_per_tensor(obf16.to_f32(w))
+    assert np.float32(sx.item()).view(np.uint32) == np.float32(want_sx).view(np.uint32)
+    assert np.float32(sw.item()).view(np.uint32) == np.float32(want_sw).view(np.uint32)
+    assert np.array_equal(xc.cpu().numpy(), want_xc)
+    assert np.array_equal(wtc.cpu().numpy(), want_wc.T)
+    print("proj full: gemm", flush=True)
+    out = rtv_lib.gemm_fp8(xc, sx, wtc, sw)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 255, 256, wl.chunk_tokens - 1],
+                                     rng.integers(0, wl.chunk_tokens, 60)]))
+    got = _np_bits(out[torch.as_tensor(rows, device=dev)])
+    _check_gemm(got, want_xc[rows], want_sx, want_wc, want_sw)
+
+    print("proj full: append from the GEMM output", flush=True)
+    cache = _proj_cache(rtv_lib, wl, 1)
+    k, v = _kv_views(out, wl)
+    assert k.stride(0) == wl.proj_width
+    cache.append(0, k, v)
+    H, D, T = wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame
+    want_qkv = ogemm.gemm_bf16(want_xc[rows], want_sx, want_wc, want_sw)
+    wk = want_qkv[:, H * D:2 * H * D].reshape(-1, H, D)
+    wv = want_qkv[:, 2 * H * D:].reshape(-1, H, D)
+    c, s = orope.cos_sin_table(rows, D, wl.rope_base)     # chunk 0: position = token index
+    wkc, wks = oquant.quantize_rows(orope.apply_rope(obf16.to_f32(wk), c, s))
+    wvc, wvs = oquant.quantize_rows(obf16.to_f32(wv))
+    gk, gks, gv, gvs = ring_rows(cache, 0, rows)           # head frame 0: slot = token
+    gq = got.reshape(len(rows), 3, H, D)
+    same_k = np.all(gq[:, 1] == wk, axis=-1)
+    same_v = np.all(gq[:, 2] == wv, axis=-1)
+    _check_rows_against_oracle(gk, gks, wkc, wks, same_k)
+    _check_rows_against_oracle(gv, gvs, wvc, wvs, same_v)
+
+
+def test_append_from_projection_layout_bit_exact(rtv_lib):
+    """Append from K/V columns of a [11968 x 4608] projection-layout buffer
+    (token stride 4608 elements): every code and scale bit for bit."""
+    wl = get_workload("proj")
+    H, D = wl.n_kv_heads, wl.head_dim
+    _, k, v = qkv_normal(wl, 0, 0, 0)
+    qkv = np.zeros((wl.chunk_tokens, 3, H, D), np.uint16)
+    qkv[:, 0] = 0x7FC0                                  # NaN in the Q columns: must not be read
+    qkv[:, 1] = k
+    qkv[:, 2] = v
+    dev_qkv = to_dev_bf16(qkv.reshape(wl.chunk_tokens, wl.proj_width))
+    kd, vd = _kv_views(dev_qkv, wl)
+    cache = _proj_cache(rtv_lib, wl, 2)
+    ora = OracleKVCache(1, H, D, wl.tokens_per_frame, wl.chunk_frames, wl.capacity_frames, wl.rope_base)
+    for step in range(2):
+        print(f"strided append step={step}", flush=True)
+        cache.append(0, kd, vd)
+        e = ora.append(0, k, v)
+        L = cache.layout(0)
+        slots = L.head_frame * wl.tokens_per_frame + np.arange(wl.chunk_tokens)
+        gk, gks, gv, gvs = ring_rows(cache, 0, slots)
+        assert np.array_equal(gk, e.k_codes) and np.array_equal(gv, e.v_codes)
+        assert np.array_equal(gks.view(np.uint32), e.k_scales.view(np.uint32))
+        assert np.array_equal(gvs.view(np.uint32), e.v_scales.view(np.uint32))
+        cache.advance(0)
+        ora.advance(0)
+
+
+def test_projection_chain_reduced_grid(rtv_lib):
+    """The whole chain at the projection workload's hidden size, heads and
+    32-frame ring on a 96-token frame: quantize X, GEMM, append the strided K/V
+    columns, attend 24 query heads over 12 KV heads; 10 steps so the ring
+    wraps.  Every output of every step is compared."""
+    wl = dataclasses.replace(get_workload("proj"), grid_h=8, grid_w=12)
+    steps = 10
+    cache = _proj_cache(rtv_lib, wl, steps)
+    ora = OracleKVCache(1, wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame, wl.chunk_frames,
+                        wl.capacity_frames, wl.rope_base)
+    H, D = wl.n_kv_heads, wl.head_dim
+    _, w = projection_inputs(wl, 0, 0)
+    wtc, sw = rtv_lib.quant_fp8_per_tensor(to_dev_bf16(np.ascontiguousarray(w.T)))
+    want_wc, want_sw = ogemm.quantize_per_tensor(obf16.to_f32(w))
+    for step in range(steps):
+        print(f"proj chain step={step}", flush=True)
+        x, _ = projection_inputs(wl, 0, step)
+        xc, sx = rtv_lib.quant_fp8_per_tensor(to_dev_bf16(x))
+        out = rtv_lib.gemm_fp8(xc, sx, wtc, sw)
+        k, v = _kv_views(out, wl)
+        cache.append(0, k, v)
+        want_xc, want_sx = ogemm.quantize_per_tensor(obf16.to_f32(x))
+        assert np.array_equal(xc.cpu().numpy(), want_xc)
+        got = _np_bits(out)
+        exact = _check_gemm(got, want_xc, want_sx, want_wc, want_sw)
+        want_qkv = obf16.from_f64(exact)        # = ogemm.gemm_bf16 of the same operands
+        wk = np.ascontiguousarray(want_qkv[:, H * D:2 * H * D].reshape(-1, H, D))
+        wv = np.ascontiguousarray(want_qkv[:, 2 * H * D:].reshape(-1, H, D))
+        e = ora.append(0, wk, wv)
+        L = cache.layout(0)
+        slots = L.head_frame * wl.tokens_per_frame + np.arange(wl.chunk_tokens)
+        gk, gks, gv, gvs = ring_rows(cache, 0, slots)
+        gq = got.reshape(-1, 3, H, D)
+        _check_rows_against_oracle(gk, gks, e.k_codes, e.k_scales, np.all(gq[:, 1] == wk, axis=-1))
+        _check_rows_against_oracle(gv, gvs, e.v_codes, e.v_scales, np.all(gq[:, 2] == wv, axis=-1))
+        q = query_normal(wl, 0, step, 0)
+        att = cache.attend(0, to_dev_bf16(q))
+        want = ora.attend(0, q)
+        mx, mean = attention_errors(bf16_to_np_f32(att), want)
+        print(f"proj chain step={step} window={ora.window_frames(0)} attention max={mx:.3e} "
+              f"mean={mean:.3e}", flush=True)
+        assert mx <= MAX_ABS and mean <= MEAN_ABS
+        cache.advance(0)
+        ora.advance(0)
+
+
+@pytest.mark.timeout(600)
+def test_gqa_full_ring_95744_keys(rtv_lib):
+    """24 query heads over 12 KV heads, 2992-token frames, 32-frame ring: 8
+    chunks fill it (the window grows to 95744 keys); codes bit-exact every
+    step, attention on sampled query rows at the first and the full window."""
+    wl = get_workload("proj")
+    cache = _proj_cache(rtv_lib, wl, 8)
+    ora = OracleKVCache(1, wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame, wl.chunk_frames,
+                        wl.capacity_frames, wl.rope_base)
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, 127, 128, wl.chunk_tokens - 1],
+                                     rng.integers(0, wl.chunk_tokens, 20)]))
+    for step in range(8):
+        print(f"gqa step={step}", flush=True)
+        q, k, v = qkv_normal(wl, 0, step, 0)
+        cache.append(0, to_dev_bf16(k), to_dev_bf16(v))
+        e = ora.append(0, k, v)
+        L = cache.layout(0)
+        slots = L.head_frame * wl.tokens_per_frame + np.arange(wl.chunk_tokens)
+        gk, gks, gv, gvs = ring_rows(cache, 0, slots)
+        assert np.array_equal(gk, e.k_codes) and np.array_equal(gv, e.v_codes)
+        assert np.array_equal(gks.view(np.uint32), e.k_scales.view(np.uint32))
+        assert np.array_equal(gvs.view(np.uint32), e.v_scales.view(np.uint32))
+        if step in (0, 7):
+            out = cache.attend(0, to_dev_bf16(q))
+            want = ora.attend(0, q, rows=rows)
+            mx, mean = attention_errors(bf16_to_np_f32(out)[rows], want)
+            print(f"gqa step={step} window={ora.window_frames(0)} attention max={mx:.3e} "
+                  f"mean={mean:.3e}", flush=True)
+            assert mx <= MAX_ABS and mean <= MEAN_ABS
+        cache.advance(0)
+        ora.advance(0)

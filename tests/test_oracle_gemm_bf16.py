@@ -64,3 +64,81 @@ def test_fp32_accumulation_within_bound():
         acc = acc + a[:, k:k + 1] * b[k:k + 1, :]     # float32, sequential
     acc = acc.astype(np.float64) * (float(sx) * float(sw))
     assert np.all(np.abs(acc - exact) <= gemm.error_bound(xc, sx, wc, sw) + 1e-30)
+
+
+def _grouped_truncation_sum(a_codes, b_codes, group=8, align_bits=13):
+    """Plain model of an FP8 dot product that aligns each group of `group`
+    consecutive products to the group's largest exponent sum and truncates
+    them toward zero to 2^(E - align_bits), then adds the groups exactly."""
+    ea = gemm.code_exponents(a_codes)
+    eb = gemm.code_exponents(b_codes)
+    a = e4m3.decode(a_codes)
+    b = e4m3.decode(b_codes)
+    M, K = a.shape
+    N = b.shape[1]
+    out = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            for g0 in range(0, K, group):
+                sl = slice(g0, g0 + group)
+                esum = ea[m, sl] + eb[sl, n]
+                if np.all(np.isneginf(esum)):
+                    continue
+                lsb = 2.0 ** (np.max(esum) - align_bits)
+                p = a[m, sl] * b[sl, n]
+                out[m, n] += np.sum(np.trunc(p / lsb) * lsb)
+    return out
+
+
+def test_code_exponents():
+    assert gemm.code_exponents(np.array([0x38]))[0] == 0         # 1.0
+    assert gemm.code_exponents(np.array([0x7E]))[0] == 8         # 448
+    assert gemm.code_exponents(np.array([0x01]))[0] == -6        # 2^-9, subnormal
+    assert gemm.code_exponents(np.array([0x08]))[0] == -6        # 2^-6, smallest normal
+    assert np.isneginf(gemm.code_exponents(np.array([0x80]))[0])
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]
+    codes = codes[(codes & 0x7F) != 0]
+    v = np.abs(e4m3.decode(codes))
+    e = gemm.code_exponents(codes)
+    normal = ((codes >> 3) & 0xF) != 0
+    assert np.all(2.0 ** e[normal] <= v[normal]) and np.all(v[normal] < 2.0 ** (e[normal] + 1))
+    assert np.all(v[~normal] < 2.0 ** e[~normal])
+
+
+def test_group_truncation_model_within_bound():
+    """The bound covers the truncating model on full-range codes (the hardest
+    case: products spread over 35 binades) and on N(0,1)-like data."""
+    rng = np.random.default_rng(7)
+    for trial in range(3):
+        a = rng.integers(0, 256, (6, 64), dtype=np.uint8)
+        b = rng.integers(0, 256, (64, 5), dtype=np.uint8)
+        a[(a & 0x7F) == 0x7F] = 0x7E
+        b[(b & 0x7F) == 0x7F] = 0x7E
+        exact = gemm.gemm_fp64(a, 1.0, b, 1.0)
+        model = _grouped_truncation_sum(a, b)
+        bound = gemm.error_bound(a, 1.0, b, 1.0)
+        assert np.all(np.abs(model - exact) <= bound)
+        # the group term is what makes it hold: the float32-only bound is too tight
+        f32_only = 64 * 2.0 ** -24 * (np.abs(e4m3.decode(a)) @ np.abs(e4m3.decode(b)))
+        if trial == 0:
+            assert np.any(np.abs(model - exact) > f32_only)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    w = rng.standard_normal((256, 3)).astype(np.float32)
+    xc, sx = gemm.quantize_per_tensor(x)
+    wc, sw = gemm.quantize_per_tensor(w)
+    model = _grouped_truncation_sum(xc, wc) * (float(sx) * float(sw))
+    exact = gemm.gemm_fp64(xc, sx, wc, sw)
+    assert np.all(np.abs(model - exact) <= gemm.error_bound(xc, sx, wc, sw))
+
+
+def test_group_truncation_model_reproduces_cancellation_cases():
+    """448 + c - 448 within one group keeps c only to multiples of 2^(8-13);
+    in different groups c survives whole."""
+    c = np.array([0x1E], np.uint8)                      # 0.109375
+    a = np.zeros((1, 16), np.uint8)
+    a[0, 0], a[0, 1], a[0, 2] = 0x7E, 0xFE, c[0]
+    b = np.full((16, 1), 0x38, np.uint8)
+    assert _grouped_truncation_sum(a, b)[0, 0] == 0.09375
+    a[0, 2], a[0, 9] = 0, c[0]
+    assert _grouped_truncation_sum(a, b)[0, 0] == 0.109375
