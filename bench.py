@@ -8,7 +8,10 @@ for one diffusion step: page "Runway: Πώς ένα AI 57 δισ. παραμέτ
 βίντεο στα 24 fps", section "Από οκτώ H100 σε τέσσερις").  Shape: 12 KV heads x
 128, 2992 tokens per frame (44x68 latent grid), 11968-token chunks, 16-frame
 ring (47872 slots).  Inputs are synthetic N(0,1) bf16 drawn on the device, one
-(Q, K, V) set per layer, resident in HBM before timing starts.
+(Q, K, V) set per layer, resident in HBM before timing starts.  Every layer's
+ring is filled before the warm-up steps, so all timed steps run in the steady
+state (full 16-frame window; the four growth steps of a fresh cache are
+cheaper and not part of the figure).
 
 Prints ONE JSON line (see --help).  The oracle leg (cpu_baseline) times the CPU
 oracle on a bounded sample of the same workload and scales it to one step.
@@ -36,12 +39,118 @@ def parse():
     p.add_argument("--layers", type=int, default=60)
     p.add_argument("--calls", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=8,
+                   help="query heads (all chunk rows) the oracle attends in the cpu_baseline sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the timed steps, copy MIB MiB device-to-device once (a kernel of "
                         "known traffic to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                    help="HBM bytes per launch from rocprofv3 counters (optional)")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="host only: summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; csv "
+                        "output) of this script with --copy-calibration into --traffic-json, then exit")
+    p.add_argument("--copy-bytes", type=int, default=1 << 30,
+                   help="bytes of the calibration copy in the --pmc runs")
     return p.parse_args()
+
+
+KERNEL_SOURCES = {
+    "attend_kernel": "kv_cache_attention_rtv_amd/csrc/attend.hip",
+    "combine_kernel": "kv_cache_attention_rtv_amd/csrc/attend.hip",
+    "append_rope_quant_kernel": "kv_cache_attention_rtv_amd/csrc/append.hip",
+}
+
+
+def source_hash(rel: str) -> str:
+    import hashlib
+
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _kernel_key(name: str):
+    import re
+
+    for k in KERNEL_SOURCES:
+        if k in name:
+            m = re.search(k + r"<[^(]*>", name)
+            return m.group(0) if m else k
+    if "copyBuffer" in name:
+        return "copy"
+    return None
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, copy_bytes: int, out_json: str):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled by
+    what the same counter reads for a device copy of known size."""
+    import csv
+    import glob
+
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no *counter_collection.csv under {d}")
+        sums = {}
+        for fn in files:
+            with open(fn, newline="") as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    key = _kernel_key(row.get("Kernel_Name", ""))
+                    if key is None:
+                        continue
+                    disp = (fn, row.get("Dispatch_Id"))
+                    sums.setdefault(key, {}).setdefault(disp, 0.0)
+                    sums[key][disp] += float(row["Counter_Value"])
+        per[counter] = {k: sum(v.values()) / len(v) for k, v in sums.items()}
+        per[counter + "_dispatches"] = {k: len(v) for k, v in sums.items()}
+    calib = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        kib = per[counter].get("copy")
+        if not kib:
+            raise SystemExit(f"no copy kernel in the {counter} run (run bench.py with --copy-calibration)")
+        calib[counter] = copy_bytes / (kib * 1024.0)
+    kernels = {}
+    for k in per["FETCH_SIZE"]:
+        if k == "copy" or k not in per["WRITE_SIZE"]:
+            continue
+        fb = per["FETCH_SIZE"][k] * 1024.0 * calib["FETCH_SIZE"]
+        wb = per["WRITE_SIZE"][k] * 1024.0 * calib["WRITE_SIZE"]
+        base = k.split("<")[0]
+        kernels[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes": round(fb + wb),
+                      "raw_fetch_kib": round(per["FETCH_SIZE"][k], 1),
+                      "raw_write_kib": round(per["WRITE_SIZE"][k], 1),
+                      "dispatches": per["FETCH_SIZE_dispatches"][k],
+                      "source": KERNEL_SOURCES[base], "source_sha256_16": source_hash(KERNEL_SOURCES[base])}
+    out = {"calibration": {"copy_bytes": copy_bytes,
+                           "fetch_factor": round(calib["FETCH_SIZE"], 4),
+                           "write_factor": round(calib["WRITE_SIZE"], 4)},
+           "kernels": kernels}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(out, sort_keys=True))
+
+
+def traffic_of(path: str, prefix: str):
+    """Calibrated HBM bytes per launch of the kernels named `prefix...` in a
+    pmc summary, or None when absent or taken from another version of the
+    kernel's source."""
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            kernels = json.load(f)["kernels"]
+    except Exception:
+        return None
+    hits = {k: v for k, v in kernels.items() if k.startswith(prefix)}
+    if not hits:
+        return None
+    for v in hits.values():
+        if v.get("source_sha256_16") != source_hash(v["source"]):
+            return None
+    return hits
 
 
 def algorithmic(wl, window_frames):
@@ -53,8 +162,10 @@ def algorithmic(wl, window_frames):
     return append_bytes, attend_flops
 
 
-def cpu_baseline(wl):
-    """Time the oracle on a bounded sample and scale it to one step."""
+def cpu_baseline(wl, heads: int):
+    """Time the oracle on a bounded sample of one call and scale it to a step:
+    the cache upkeep (RoPE + e4m3) of a whole chunk, and float64 attention of
+    every query row of `heads` heads (1024-row blocks) over a full window."""
     import numpy as np
 
     from oracle import attention, bf16, quant, rope
@@ -66,39 +177,41 @@ def cpu_baseline(wl):
     except Exception:
         blas_threads = os.cpu_count() or 1
     q, k, v = qkv_normal(wl, 0, 0, 0)
-    T, F, C = wl.tokens_per_frame, wl.chunk_frames, wl.capacity_frames
-    # (a) cache upkeep for one frame's tokens (all heads), x F frames per call
+    T, F, C, D = wl.tokens_per_frame, wl.chunk_frames, wl.capacity_frames, wl.head_dim
+    n = wl.chunk_tokens
     t0 = time.perf_counter()
-    pos = np.arange(12 * T, 13 * T)
-    c, s = rope.cos_sin_table(pos, wl.head_dim, wl.rope_base)
-    kr = rope.apply_rope(bf16.to_f32(k[:T]), c, s)
-    kc, ks = quant.quantize_rows(kr)
-    vc, vs = quant.quantize_rows(bf16.to_f32(v[:T]))
-    t_append = (time.perf_counter() - t0) * F
-    # (b) attention: 128 query rows of one head over a full window of C*T keys
+    pos = np.arange(C * T, C * T + n)
+    c, s = rope.cos_sin_table(pos, D, wl.rope_base)
+    quant.quantize_rows(rope.apply_rope(bf16.to_f32(k), c, s))
+    quant.quantize_rows(bf16.to_f32(v))
+    t_append = time.perf_counter() - t0
     rng = np.random.default_rng(1)
-    kd = quant.dequantize_rows(*quant.quantize_rows(
-        rng.standard_normal((C * T, wl.head_dim)).astype(np.float32)))
-    vd = quant.dequantize_rows(*quant.quantize_rows(
-        rng.standard_normal((C * T, wl.head_dim)).astype(np.float32)))
-    rows = 256
-    qr = rope.apply_rope(bf16.to_f32(q[:rows, :1]), c[:rows], s[:rows])[:, 0]
+    kd = quant.dequantize_rows(*quant.quantize_rows(rng.standard_normal((C * T, D)).astype(np.float32)))
+    vd = quant.dequantize_rows(*quant.quantize_rows(rng.standard_normal((C * T, D)).astype(np.float32)))
+    heads = max(1, min(heads, wl.n_q_heads))
     t0 = time.perf_counter()
-    attention.attend_rows(qr, kd, vd)
-    t_rows = time.perf_counter() - t0
-    t_attend = t_rows * (wl.chunk_tokens * wl.n_q_heads / rows)
-    step_ms = (t_append + t_attend) * wl.n_layers * wl.calls_per_layer * 1e3
+    for h in range(heads):
+        qr = rope.apply_rope(bf16.to_f32(q[:, h:h + 1]), c, s)[:, 0]
+        for r0 in range(0, n, 1024):
+            attention.attend_rows(qr[r0:r0 + 1024], kd, vd)
+    t_heads = time.perf_counter() - t0
+    t_attend = t_heads * wl.n_q_heads / heads
+    calls = wl.n_layers * wl.calls_per_layer
+    step_ms = (t_append + t_attend) * calls * 1e3
     return {
         "value": round(step_ms, 1), "unit": "ms/step", "cores": int(blas_threads), "kind": "oracle",
-        "sample": (f"oracle RoPE+e4m3 upkeep of one frame ({T} tokens x {wl.n_kv_heads} heads) x {F}, "
-                   f"and float64 attention of {rows} query rows of one head over {C * T} keys, "
-                   f"scaled to {wl.chunk_tokens}x{wl.n_q_heads} rows and "
-                   f"{wl.n_layers * wl.calls_per_layer} calls per step"),
+        "sample": (f"one call measured: oracle RoPE+e4m3 upkeep of the {n}-token chunk x {wl.n_kv_heads} "
+                   f"heads ({t_append:.2f} s) and float64 attention of all {n} query rows of {heads} of "
+                   f"{wl.n_q_heads} heads over {C * T} keys ({t_heads:.2f} s); scaled to {wl.n_q_heads} heads "
+                   f"and {calls} calls per step; cores = numpy BLAS threads (elementwise steps use one)"),
     }
 
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_bytes, args.traffic_json)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path has no "
               "multi-GPU mode", file=sys.stderr)
@@ -114,7 +227,7 @@ def main():
     wl = dataclasses.replace(get_workload("step"), n_layers=args.layers, calls_per_layer=args.calls)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    total_steps = args.warmup + args.steps
+    total_steps = wl.capacity_frames // wl.chunk_frames + args.warmup + args.steps
     cfg = rtv.RtvConfig(wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
                         wl.tokens_per_frame, wl.chunk_frames, wl.capacity_frames,
                         (total_steps + 1) * wl.chunk_frames, wl.rope_base)
@@ -145,6 +258,12 @@ def main():
                     events[2][-1].record(stream)
         cache.advance(-1, stream=stream)
 
+    # steady state: fill every layer's ring before the warm-up, so every timed
+    # (and warm-up) attend sees the full window
+    for _ in range(wl.capacity_frames // wl.chunk_frames):
+        for layer in range(wl.n_layers):
+            cache.append(layer, inputs[layer][1], inputs[layer][2], stream=stream)
+        cache.advance(-1, stream=stream)
     windows = []
     for s in range(args.warmup):
         run_step()
@@ -174,13 +293,17 @@ def main():
     app_avg_ms = sum(app_ms) / len(app_ms)
     app_gbs = app_bytes / (app_avg_ms * 1e-3) / 1e9
 
+    # HBM bytes per rtv_attend call (attention + combine kernels of the
+    # steady-state window) and per append, from the calibrated counters
+    att_traffic = traffic_of(args.traffic_json, "attend_kernel<128, false, false, false>")
+    comb_traffic = traffic_of(args.traffic_json, "combine_kernel<128>")
+    app_traffic = traffic_of(args.traffic_json, "append_rope_quant_kernel<128>")
     traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            with open(args.traffic_json) as f:
-                traffic = json.load(f).get("attend_bytes_per_launch")
-        except Exception:
-            traffic = None
+    if att_traffic:
+        traffic = sum(v["bytes"] for v in att_traffic.values())
+        if comb_traffic:
+            traffic += sum(v["bytes"] for v in comb_traffic.values())
+    app_bytes_measured = sum(v["bytes"] for v in app_traffic.values()) if app_traffic else None
 
     result = {
         "metric": "ms/step for 240 append+attend calls (1-GPU head share); HBM GB/s, FP8 MFMA %",
@@ -203,7 +326,8 @@ def main():
             "parallelism": "none (one GPU's head share)",
         },
         "roofline": {
-            "bound": "mfma", "kernel": "attend_kernel<128>",
+            "bound": "mfma",
+            "kernel": "rtv_attend = attend_kernel<128, false, false, false> + combine_kernel<128>",
             "achieved": round(att_tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
             "avg_launch_ms": round(att_avg_ms, 4),
@@ -213,7 +337,7 @@ def main():
             "bound": "hbm", "kernel": "append_rope_quant_kernel<128>",
             "achieved": round(app_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(app_gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(app_avg_ms, 5),
-            "bytes_per_launch": app_bytes,
+            "bytes_per_launch": app_bytes, "traffic": app_bytes_measured,
         },
         "wall_s_timed": round(wall, 3),
     }
@@ -226,7 +350,7 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = nb
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
     print(json.dumps(result), flush=True)
 
 
