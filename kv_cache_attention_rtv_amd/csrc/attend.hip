@@ -6,12 +6,15 @@
 // τέσσερις"; the cache holds RoPE-rotated e4m3 K and e4m3 V, page "Runway
 // explains how it serves a 57B video model in real time", fourth paragraph).
 //
-// Work decomposition: one workgroup = 256 queries of one query head, 4 waves
-// of 64 queries, each wave two 32-query sub-tiles that share every K and V
-// operand it reads from LDS (half the LDS traffic of one sub-tile per wave).
-// The workgroup walks 64-key tiles of the window's (at most two) slot
-// segments through a 3-stage LDS ring with one barrier per tile; the global
-// loads of tile t+3 are in flight while tile t is computed.
+// Work decomposition: one workgroup = 256 queries of one query head, 8 waves
+// of 32 queries, one workgroup per CU.  Waves w and w + 4 share a SIMD and,
+// held together by the per-tile barrier, run their softmax at the same time:
+// a lone wave issues VALU instructions at about half the SIMD's rate, so two
+// waves in the same phase keep the VALU busy while the matrix-core phases of
+// both follow back to back.  The workgroup walks 64-key tiles of the
+// window's (at most two) slot segments through a 3-stage LDS ring with one
+// barrier per tile; waves 0-3 stage the K rows and waves 4-7 the V rows of
+// tile t+2 while tile t is computed.
 //
 // Per wave, tile and sub-tile, with v_mfma_f32_32x32x64_f8f6f4 (e4m3, f32 acc):
 //   S^T[key][query] = K . Q^T            2 key halves x D/64 k-steps
@@ -35,7 +38,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kSub = 1;                     // 32-query sub-tiles per wave
 constexpr int kQPW = 32 * kSub;             // queries per wave
@@ -94,9 +97,10 @@ struct Smem {
   static constexpr int STAGE = K_BYTES + V_BYTES + 2 * 64 * 4;   // + kf, wf
 };
 
-// staged tile: D/4 bytes of K and of V per thread (two 16 B pieces for D=128)
+// staged tile: threads 0..255 (waves 0-3) move the K rows and kf, threads
+// 256..511 (waves 4-7) the transposed V rows and wf; D/4 bytes each
 struct TileRegs {
-  uint4 k0, k1, v0, v1;
+  uint4 c0, c1;
   float s;
 };
 
@@ -110,28 +114,35 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const u
                                           const uint8_t* vc, const float* ks, const float* vs,
                                           int tid) {
   constexpr int LD_BYTES = D / 4;
-  const uint8_t* kt = kc + (int64_t)t.tile * 64 * D;
-  const uint8_t* vt = vc + (int64_t)t.tile * 64 * D;
-  r.k0 = *(const uint4*)(kt + tid * LD_BYTES);
-  r.v0 = *(const uint4*)(vt + tid * LD_BYTES);
-  if constexpr (LD_BYTES == 32) {
-    r.k1 = *(const uint4*)(kt + tid * LD_BYTES + 16);
-    r.v1 = *(const uint4*)(vt + tid * LD_BYTES + 16);
-  }
-  const float* src = tid < 64 ? ks : vs;
-  r.s = tid < 128 ? src[(int64_t)t.tile * 64 + (tid & 63)] : 0.0f;
+  const bool isv = tid >= 256;
+  const int gt = tid & 255;
+  const uint8_t* src = (isv ? vc : kc) + (int64_t)t.tile * 64 * D + gt * LD_BYTES;
+  r.c0 = *(const uint4*)(src);
+  if constexpr (LD_BYTES == 32) r.c1 = *(const uint4*)(src + 16);
+  // every thread loads a scale (only 64 per half are used): no lane branch
+  r.s = (isv ? vs : ks)[(int64_t)t.tile * 64 + (gt & 63)];
 }
 
+// K piece of 16 bytes at byte b of the tile (row = key b / D); V piece at
+// byte b of the transposed tile (row = d, col = slot position).  Keys of a
+// partial tile outside the segment get zero codes (they may hold anything,
+// NaN codes included).
 template <int D, bool MASK>
-__device__ __forceinline__ void store_piece(uint4 kq, uint4 v, int b, uint8_t* st, bool partial,
-                                            int base, int lo, int hi) {
+__device__ __forceinline__ void store_k_piece(uint4 q, int b, uint8_t* st, bool partial, int base,
+                                              int lo, int hi) {
+  using SM = Smem<D>;
+  if (MASK && partial) {
+    const int kslot = base + b / D;
+    if (!(kslot >= lo && kslot < hi)) q = make_uint4(0, 0, 0, 0);
+  }
+  *(uint4*)(st + (b / D) * SM::KROW + (b % D)) = q;
+}
+template <int D, bool MASK>
+__device__ __forceinline__ void store_v_piece(uint4 v, int b, uint8_t* st, bool partial, int base,
+                                              int lo, int hi) {
   using SM = Smem<D>;
   const int row = b / 64, col = b % 64;
   if (MASK && partial) {
-    // zero the codes of keys outside the segment (they may hold anything,
-    // NaN codes included): the K row of such a key, and its V bytes
-    const int kslot = base + b / D;
-    if (!(kslot >= lo && kslot < hi)) kq = make_uint4(0, 0, 0, 0);
     uint32_t m[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -144,7 +155,6 @@ __device__ __forceinline__ void store_piece(uint4 kq, uint4 v, int b, uint8_t* s
     }
     v.x &= m[0]; v.y &= m[1]; v.z &= m[2]; v.w &= m[3];
   }
-  *(uint4*)(st + (b / D) * SM::KROW + (b % D)) = kq;
   *(uint4*)(st + SM::K_BYTES + row * SM::VROW + col) = v;
 }
 
@@ -154,21 +164,26 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, 
                                            float kscale, float wscale, int tid) {
   using SM = Smem<D>;
   constexpr int LD_BYTES = D / 4;
+  const bool isv = tid >= 256;
+  const int gt = tid & 255;
   const int base = t.tile * 64;
   const bool partial = t.lo > base || t.hi < base + 64;
-  store_piece<D, MASK>(r.k0, r.v0, tid * LD_BYTES, st, partial, base, t.lo, t.hi);
-  if constexpr (LD_BYTES == 32)
-    store_piece<D, MASK>(r.k1, r.v1, tid * LD_BYTES + 16, st, partial, base, t.lo, t.hi);
+  const int b = gt * LD_BYTES;
+  if (isv) {
+    store_v_piece<D, MASK>(r.c0, b, st, partial, base, t.lo, t.hi);
+    if constexpr (LD_BYTES == 32) store_v_piece<D, MASK>(r.c1, b + 16, st, partial, base, t.lo, t.hi);
+  } else {
+    store_k_piece<D, MASK>(r.c0, b, st, partial, base, t.lo, t.hi);
+    if constexpr (LD_BYTES == 32) store_k_piece<D, MASK>(r.c1, b + 16, st, partial, base, t.lo, t.hi);
+  }
   float* kf = (float*)(st + SM::K_BYTES + SM::V_BYTES);
-  float* wf = kf + 64;
-  if (tid < 128) {
-    const int key = tid & 63;
-    const int slot = base + key;
+  if (gt < 64) {
+    const int slot = base + gt;
     const bool ok = !MASK || (slot >= t.lo && slot < t.hi);
     // a key outside the segment gets kf = kMaskFactor: its raw score is the
     // bias -448*448 added by the masking MFMA, so t ~ -2e35 and p = 0
-    if (tid < 64) kf[key] = ok ? r.s * kscale : kMaskFactor;
-    else wf[key] = ok ? r.s * wscale : 0.0f;
+    if (isv) kf[64 + gt] = ok ? r.s * wscale : 0.0f;
+    else kf[gt] = ok ? r.s * kscale : kMaskFactor;
   }
 }
 
@@ -269,7 +284,7 @@ __device__ __forceinline__ v8i softmax_tile(const v16f (&s)[2], const float* kf,
 // by large K channels: short windows always carry QLO, longer ones when the
 // cache was created for two query terms (keys with outlier channels).
 template <int D, bool MASK, bool QLO, bool PLO>
-__global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void attend_kernel(AttendArgs a) {
   using SM = Smem<D>;
   constexpr int NSTEP = D / 64;             // MFMA k-steps for K.Q^T
   constexpr int NDT = D / 32;               // 32-row d sub-tiles of O^T
@@ -532,10 +547,14 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
       }
     }
 
+    // staging of tile it + 2 (stored) and it + 3 (loaded), unconditional with
+    // the tile index clamped (past the end the copy lands in a stage nobody
+    // reads again), so that it shares a basic block with the PV products
     const int nst = stage + 2 >= kStages ? stage + 2 - kStages : stage + 2;
-    if (it + kStages - 1 < n_it)
-      store_tile<D, MASK>(regs, tref(it + kStages - 1), smem + nst * SM::STAGE, kscale, cP, tid);
-    if (it + kStages < n_it) load_tile<D>(regs, tref(it + kStages), kc, vc, ks, vs, tid);
+    const int ts = it + kStages - 1 < n_it ? it + kStages - 1 : n_it - 1;
+    const int tl = it + kStages < n_it ? it + kStages : n_it - 1;
+    store_tile<D, MASK>(regs, tref(ts), smem + nst * SM::STAGE, kscale, cP, tid);
+    load_tile<D>(regs, tref(tl), kc, vc, ks, vs, tid);
     __syncthreads();
     stage = stage + 1 == kStages ? 0 : stage + 1;
   }
@@ -581,7 +600,7 @@ __global__ __launch_bounds__(kThreads, 2) void attend_kernel(AttendArgs a) {
 // Merge the key-range parts of the split units: for each query,
 // M = max_p m_p, w_p = 2^(m_p - M), O = sum_p w_p O_p / sum_p w_p l_p.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
+__global__ __launch_bounds__(2 * kQPB) void combine_kernel(AttendArgs a) {
   const int r = blockIdx.x;                       // split unit r
   const int unit = a.n_full + r;
   const int head = unit / a.n_qtiles;
@@ -627,7 +646,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
 int attend_queries_per_block() { return kQPB; }
 
 // parts are bounded so that the workspace has a fixed size
-constexpr int kMaxParts = 1024;
+constexpr int kMaxParts = 512;
 int attend_max_parts() { return kMaxParts; }
 size_t attend_workspace_bytes(int head_dim) {
   return (size_t)kMaxParts * kQPB * ((size_t)head_dim + 2) * sizeof(float);
@@ -698,9 +717,9 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || rem == 0) return e;
   if (head_dim == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, dim3(rem), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(combine_kernel<128>, dim3(rem), dim3(2 * kQPB), 0, stream, args);
   else
-    hipLaunchKernelGGL(combine_kernel<64>, dim3(rem), dim3(256), 0, stream, args);
+    hipLaunchKernelGGL(combine_kernel<64>, dim3(rem), dim3(2 * kQPB), 0, stream, args);
   return hipGetLastError();
 }
 
