@@ -38,12 +38,21 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 8;
+#ifndef RTV_ATTEND_WAVES
+#define RTV_ATTEND_WAVES 8
+#endif
+#ifndef RTV_ATTEND_STAGES
+#define RTV_ATTEND_STAGES 3
+#endif
+#ifndef RTV_ATTEND_WG_PER_CU
+#define RTV_ATTEND_WG_PER_CU 1
+#endif
+constexpr int kWaves = RTV_ATTEND_WAVES;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kSub = 1;                     // 32-query sub-tiles per wave
 constexpr int kQPW = 32 * kSub;             // queries per wave
 constexpr int kQPB = kWaves * kQPW;         // queries per workgroup
-constexpr int kStages = 3;
+constexpr int kStages = RTV_ATTEND_STAGES;
 constexpr float kTau = 3.0f;
 constexpr float kPmax = 440.0f;             // bound on P' (below the e4m3 max 448)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -97,11 +106,13 @@ struct Smem {
   static constexpr int STAGE = K_BYTES + V_BYTES + 2 * 64 * 4;   // + kf, wf
 };
 
-// staged tile: threads 0..255 (waves 0-3) move the K rows and kf, threads
-// 256..511 (waves 4-7) the transposed V rows and wf; D/4 bytes each
+// Staged tile: with 512 threads, threads 0..255 (waves 0-3) move the K rows
+// and kf, threads 256..511 (waves 4-7) the transposed V rows and wf; with
+// 256 threads every thread moves a K piece and a V piece.  D/4 bytes each.
+constexpr int kStageJobs = kThreads >= 512 ? 1 : 2;
 struct TileRegs {
-  uint4 c0, c1;
-  float s;
+  uint4 c[kStageJobs][2];
+  float s[kStageJobs];
 };
 
 struct TileRef {
@@ -114,13 +125,16 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const u
                                           const uint8_t* vc, const float* ks, const float* vs,
                                           int tid) {
   constexpr int LD_BYTES = D / 4;
-  const bool isv = tid >= 256;
   const int gt = tid & 255;
-  const uint8_t* src = (isv ? vc : kc) + (int64_t)t.tile * 64 * D + gt * LD_BYTES;
-  r.c0 = *(const uint4*)(src);
-  if constexpr (LD_BYTES == 32) r.c1 = *(const uint4*)(src + 16);
-  // every thread loads a scale (only 64 per half are used): no lane branch
-  r.s = (isv ? vs : ks)[(int64_t)t.tile * 64 + (gt & 63)];
+#pragma unroll
+  for (int j = 0; j < kStageJobs; ++j) {
+    const bool isv = kStageJobs == 1 ? tid >= 256 : j == 1;
+    const uint8_t* src = (isv ? vc : kc) + (int64_t)t.tile * 64 * D + gt * LD_BYTES;
+    r.c[j][0] = *(const uint4*)(src);
+    if constexpr (LD_BYTES == 32) r.c[j][1] = *(const uint4*)(src + 16);
+    // every thread loads a scale (only 64 per job are used): no lane branch
+    r.s[j] = (isv ? vs : ks)[(int64_t)t.tile * 64 + (gt & 63)];
+  }
 }
 
 // K piece of 16 bytes at byte b of the tile (row = key b / D); V piece at
@@ -164,26 +178,29 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, 
                                            float kscale, float wscale, int tid) {
   using SM = Smem<D>;
   constexpr int LD_BYTES = D / 4;
-  const bool isv = tid >= 256;
   const int gt = tid & 255;
   const int base = t.tile * 64;
   const bool partial = t.lo > base || t.hi < base + 64;
   const int b = gt * LD_BYTES;
-  if (isv) {
-    store_v_piece<D, MASK>(r.c0, b, st, partial, base, t.lo, t.hi);
-    if constexpr (LD_BYTES == 32) store_v_piece<D, MASK>(r.c1, b + 16, st, partial, base, t.lo, t.hi);
-  } else {
-    store_k_piece<D, MASK>(r.c0, b, st, partial, base, t.lo, t.hi);
-    if constexpr (LD_BYTES == 32) store_k_piece<D, MASK>(r.c1, b + 16, st, partial, base, t.lo, t.hi);
-  }
   float* kf = (float*)(st + SM::K_BYTES + SM::V_BYTES);
-  if (gt < 64) {
-    const int slot = base + gt;
-    const bool ok = !MASK || (slot >= t.lo && slot < t.hi);
-    // a key outside the segment gets kf = kMaskFactor: its raw score is the
-    // bias -448*448 added by the masking MFMA, so t ~ -2e35 and p = 0
-    if (isv) kf[64 + gt] = ok ? r.s * wscale : 0.0f;
-    else kf[gt] = ok ? r.s * kscale : kMaskFactor;
+#pragma unroll
+  for (int j = 0; j < kStageJobs; ++j) {
+    const bool isv = kStageJobs == 1 ? tid >= 256 : j == 1;
+    if (isv) {
+      store_v_piece<D, MASK>(r.c[j][0], b, st, partial, base, t.lo, t.hi);
+      if constexpr (LD_BYTES == 32) store_v_piece<D, MASK>(r.c[j][1], b + 16, st, partial, base, t.lo, t.hi);
+    } else {
+      store_k_piece<D, MASK>(r.c[j][0], b, st, partial, base, t.lo, t.hi);
+      if constexpr (LD_BYTES == 32) store_k_piece<D, MASK>(r.c[j][1], b + 16, st, partial, base, t.lo, t.hi);
+    }
+    if (gt < 64) {
+      const int slot = base + gt;
+      const bool ok = !MASK || (slot >= t.lo && slot < t.hi);
+      // a key outside the segment gets kf = kMaskFactor: its raw score is the
+      // bias -448*448 added by the masking MFMA, so t ~ -2e35 and p = 0
+      if (isv) kf[64 + gt] = ok ? r.s[j] * wscale : 0.0f;
+      else kf[gt] = ok ? r.s[j] * kscale : kMaskFactor;
+    }
   }
 }
 
@@ -284,7 +301,7 @@ __device__ __forceinline__ v8i softmax_tile(const v16f (&s)[2], const float* kf,
 // by large K channels: short windows always carry QLO, longer ones when the
 // cache was created for two query terms (keys with outlier channels).
 template <int D, bool MASK, bool QLO, bool PLO>
-__global__ __launch_bounds__(kThreads, 1) void attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(AttendArgs a) {
   using SM = Smem<D>;
   constexpr int NSTEP = D / 64;             // MFMA k-steps for K.Q^T
   constexpr int NDT = D / 32;               // 32-row d sub-tiles of O^T
@@ -547,10 +564,10 @@ __global__ __launch_bounds__(kThreads, 1) void attend_kernel(AttendArgs a) {
       }
     }
 
-    // staging of tile it + 2 (stored) and it + 3 (loaded), unconditional with
+    // staging of tile it + kStages - 1 (stored) and it + kStages (loaded), unconditional with
     // the tile index clamped (past the end the copy lands in a stage nobody
     // reads again), so that it shares a basic block with the PV products
-    const int nst = stage + 2 >= kStages ? stage + 2 - kStages : stage + 2;
+    const int nst = (stage + kStages - 1) % kStages;   // stage of tile it + kStages - 1
     const int ts = it + kStages - 1 < n_it ? it + kStages - 1 : n_it - 1;
     const int tl = it + kStages < n_it ? it + kStages : n_it - 1;
     store_tile<D, MASK>(regs, tref(ts), smem + nst * SM::STAGE, kscale, cP, tid);
