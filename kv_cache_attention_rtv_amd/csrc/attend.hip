@@ -41,18 +41,17 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 #ifndef RTV_ATTEND_WAVES
 #define RTV_ATTEND_WAVES 8
 #endif
-#ifndef RTV_ATTEND_STAGES
-#define RTV_ATTEND_STAGES 3
+#ifndef RTV_ATTEND_SCHED
+#define RTV_ATTEND_SCHED 0
 #endif
 #ifndef RTV_ATTEND_WG_PER_CU
 #define RTV_ATTEND_WG_PER_CU 1
 #endif
 constexpr int kWaves = RTV_ATTEND_WAVES;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kSub = 1;                     // 32-query sub-tiles per wave
-constexpr int kQPW = 32 * kSub;             // queries per wave
+constexpr int kQPW = 32;                    // queries per wave
 constexpr int kQPB = kWaves * kQPW;         // queries per workgroup
-constexpr int kStages = RTV_ATTEND_STAGES;
+constexpr int kStages = 4;                  // LDS ring: tiles it - 1 .. it + 2
 constexpr float kTau = 3.0f;
 constexpr float kPmax = 440.0f;             // bound on P' (below the e4m3 max 448)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -137,42 +136,46 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const u
   }
 }
 
-// K piece of 16 bytes at byte b of the tile (row = key b / D); V piece at
-// byte b of the transposed tile (row = d, col = slot position).  Keys of a
-// partial tile outside the segment get zero codes (they may hold anything,
-// NaN codes included).
-template <int D, bool MASK>
-__device__ __forceinline__ void store_k_piece(uint4 q, int b, uint8_t* st, bool partial, int base,
-                                              int lo, int hi) {
+// Byte offset in a stage of the 16-byte piece at byte b of a staged tile: K
+// rows (row = key b / D), or the transposed V rows (row = d, col = slot
+// position).
+template <int D>
+__device__ __forceinline__ int k_piece_at(int b) {
   using SM = Smem<D>;
-  if (MASK && partial) {
-    const int kslot = base + b / D;
-    if (!(kslot >= lo && kslot < hi)) q = make_uint4(0, 0, 0, 0);
-  }
-  *(uint4*)(st + (b / D) * SM::KROW + (b % D)) = q;
+  return (b / D) * SM::KROW + (b % D);
 }
-template <int D, bool MASK>
-__device__ __forceinline__ void store_v_piece(uint4 v, int b, uint8_t* st, bool partial, int base,
-                                              int lo, int hi) {
+template <int D>
+__device__ __forceinline__ int v_piece_at(int b) {
   using SM = Smem<D>;
-  const int row = b / 64, col = b % 64;
-  if (MASK && partial) {
-    uint32_t m[4];
+  return SM::K_BYTES + (b / 64) * SM::VROW + (b % 64);
+}
+// Keys of a partial tile outside the segment get zero codes (they may hold
+// anything, NaN codes included).
+template <int D>
+__device__ __forceinline__ uint4 mask_k_piece(uint4 q, int b, int base, int lo, int hi) {
+  const int kslot = base + b / D;
+  return (kslot >= lo && kslot < hi) ? q : make_uint4(0, 0, 0, 0);
+}
+__device__ __forceinline__ uint4 mask_v_piece(uint4 v, int b, int base, int lo, int hi) {
+  const int col = b % 64;
+  uint32_t m[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      m[w] = 0;
+  for (int w = 0; w < 4; ++w) {
+    m[w] = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int slot = base + vt_key(col + 4 * w + e);
-        if (slot >= lo && slot < hi) m[w] |= 0xFFu << (8 * e);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int slot = base + vt_key(col + 4 * w + e);
+      if (slot >= lo && slot < hi) m[w] |= 0xFFu << (8 * e);
     }
-    v.x &= m[0]; v.y &= m[1]; v.z &= m[2]; v.w &= m[3];
   }
-  *(uint4*)(st + SM::K_BYTES + row * SM::VROW + col) = v;
+  v.x &= m[0]; v.y &= m[1]; v.z &= m[2]; v.w &= m[3];
+  return v;
 }
 
-// kscale = s_q * log2(e) / sqrt(D); wscale = c
+// kscale = s_q * log2(e) / sqrt(D); wscale = c.  Branch-free apart from the
+// masking of partial tiles: K and V pieces differ only in their address, and
+// every thread writes the kf or wf entry of key (thread & 63); the threads
+// that share a key hold the same scale and write the same value.
 template <int D, bool MASK>
 __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, uint8_t* st,
                                            float kscale, float wscale, int tid) {
@@ -180,27 +183,26 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, 
   constexpr int LD_BYTES = D / 4;
   const int gt = tid & 255;
   const int base = t.tile * 64;
-  const bool partial = t.lo > base || t.hi < base + 64;
+  const bool partial = MASK && (t.lo > base || t.hi < base + 64);
   const int b = gt * LD_BYTES;
   float* kf = (float*)(st + SM::K_BYTES + SM::V_BYTES);
+  const int key = gt & 63;
+  const bool ok = !MASK || (base + key >= t.lo && base + key < t.hi);
 #pragma unroll
   for (int j = 0; j < kStageJobs; ++j) {
     const bool isv = kStageJobs == 1 ? tid >= 256 : j == 1;
-    if (isv) {
-      store_v_piece<D, MASK>(r.c[j][0], b, st, partial, base, t.lo, t.hi);
-      if constexpr (LD_BYTES == 32) store_v_piece<D, MASK>(r.c[j][1], b + 16, st, partial, base, t.lo, t.hi);
-    } else {
-      store_k_piece<D, MASK>(r.c[j][0], b, st, partial, base, t.lo, t.hi);
-      if constexpr (LD_BYTES == 32) store_k_piece<D, MASK>(r.c[j][1], b + 16, st, partial, base, t.lo, t.hi);
+#pragma unroll
+    for (int h = 0; h < LD_BYTES / 16; ++h) {
+      const int bb = b + 16 * h;
+      uint4 q = r.c[j][h];
+      if (partial) q = isv ? mask_v_piece(q, bb, base, t.lo, t.hi) : mask_k_piece<D>(q, bb, base, t.lo, t.hi);
+      *(uint4*)(st + (isv ? v_piece_at<D>(bb) : k_piece_at<D>(bb))) = q;
     }
-    if (gt < 64) {
-      const int slot = base + gt;
-      const bool ok = !MASK || (slot >= t.lo && slot < t.hi);
-      // a key outside the segment gets kf = kMaskFactor: its raw score is the
-      // bias -448*448 added by the masking MFMA, so t ~ -2e35 and p = 0
-      if (isv) kf[64 + gt] = ok ? r.s[j] * wscale : 0.0f;
-      else kf[gt] = ok ? r.s[j] * kscale : kMaskFactor;
-    }
+    // a key outside the segment gets kf = kMaskFactor: its raw score is the
+    // bias -448*448 added by the masking MFMA, so t ~ -2e35 and p = 0
+    const float kv = ok ? r.s[j] * kscale : kMaskFactor;
+    const float wv = ok ? r.s[j] * wscale : 0.0f;
+    kf[(isv ? 64 : 0) + key] = isv ? wv : kv;
   }
 }
 
@@ -229,12 +231,12 @@ __device__ __forceinline__ void scores(const v16f (&s)[2], const float* kf, int 
     }
 }
 
-// Softmax of one 32-query sub-tile over one 64-key tile: consumes the raw
-// scores, updates (m, l, O), returns the e4m3 P' operand.
-template <int NDT, bool PRECISE>
-__device__ __forceinline__ v8i softmax_tile(const v16f (&s)[2], const float* kf, const float* wf,
-                                            int hh, float& m, float& l, v16f (&o)[NDT], v8i& plo) {
-  float t[32];
+// Softmax of one 32-query tile over one 64-key tile, first half: t = score - m
+// for the lane's 32 keys, with the lazy running-max update (rare: rescales l
+// and the O accumulator).
+template <int NDT>
+__device__ __forceinline__ void softmax_scores(const v16f (&s)[2], const float* kf, int hh, float& m,
+                                               float& l, v16f (&o)[NDT], float (&t)[32]) {
   scores(s, kf, hh, m, t);
   float mx = -INFINITY;
 #pragma unroll
@@ -257,6 +259,13 @@ __device__ __forceinline__ v8i softmax_tile(const v16f (&s)[2], const float* kf,
     for (int j = 0; j < 32; ++j) t[j] -= m_new;
     m = m_new;
   }
+}
+
+// Second half: p = 2^t, l += p, and the e4m3 P' = p * w_key, the B operand of
+// the PV product (PRECISE: as two terms).
+template <bool PRECISE>
+__device__ __forceinline__ v8i softmax_probs(const float (&t)[32], const float* wf, int hh, float& l,
+                                             v8i& plo) {
   v8i pop;
   uint32_t prev = 0;
 #pragma unroll
@@ -347,30 +356,25 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
       svmax = __builtin_fmaxf(svmax, vs[slot]);
 
   // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
-  int q_rows[kSub];
+  const int q_row = qtile * kQPB + wave * kQPW + li;
+  const int src_row = q_row < a.n_tokens ? q_row : a.n_tokens - 1;
+  const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
+  const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
   float qamax = 0.0f;
 #pragma unroll
-  for (int sub = 0; sub < kSub; ++sub) {
-    const int row = qtile * kQPB + wave * kQPW + sub * 32 + li;
-    q_rows[sub] = row;
-    const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
-    const uint16_t* src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
-    const float* cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
+  for (int j = 0; j < P; j += 8) {
+    const uint4 w0 = *(const uint4*)(q_src + P * hh + j);
+    const uint4 w1 = *(const uint4*)(q_src + D / 2 + P * hh + j);
+    const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
+    const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-    for (int j = 0; j < P; j += 8) {
-      const uint4 w0 = *(const uint4*)(src + P * hh + j);
-      const uint4 w1 = *(const uint4*)(src + D / 2 + P * hh + j);
-      const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
-      const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
-        const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
-        const float2 c = *(const float2*)(cs + 2 * (j + e));
-        const float r0 = x0 * c.x - x1 * c.y;
-        const float r1 = x1 * c.x + x0 * c.y;
-        qamax = __builtin_fmaxf(qamax, __builtin_fmaxf(fabsf(r0), fabsf(r1)));
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
+      const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
+      const float2 c = *(const float2*)(q_cs + 2 * (j + e));
+      const float r0 = x0 * c.x - x1 * c.y;
+      const float r1 = x1 * c.x + x0 * c.y;
+      qamax = __builtin_fmaxf(qamax, __builtin_fmaxf(fabsf(r0), fabsf(r1)));
     }
   }
 #pragma unroll
@@ -397,26 +401,21 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   // ---- Q prologue pass 2: e4m3 codes in the B-operand layout ---------------
   // operand step s, byte b <-> d: D=128: d = 64 s + 32 hh + b; D=64: byte b < 16
   // -> d = 16 hh + b, b >= 16 -> d = 32 + 16 hh + b - 16 (RoPE pairs stay in-lane)
-  v8i qop[kSub][NSTEP];
-  v8i qlo[kSub][NSTEP];
-#pragma unroll
-  for (int sub = 0; sub < kSub; ++sub) {
-    const int row = q_rows[sub];
-    const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
-    const uint16_t* src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
-    const float* cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
+  v8i qop[NSTEP];
+  v8i qlo[NSTEP];
+  {
     float r0[P], r1[P];
 #pragma unroll
     for (int j = 0; j < P; j += 8) {
-      const uint4 w0 = *(const uint4*)(src + P * hh + j);
-      const uint4 w1 = *(const uint4*)(src + D / 2 + P * hh + j);
+      const uint4 w0 = *(const uint4*)(q_src + P * hh + j);
+      const uint4 w1 = *(const uint4*)(q_src + D / 2 + P * hh + j);
       const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
       const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
         const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
-        const float2 c = *(const float2*)(cs + 2 * (j + e));
+        const float2 c = *(const float2*)(q_cs + 2 * (j + e));
         r0[j + e] = (x0 * c.x - x1 * c.y) * q_inv;
         r1[j + e] = (x1 * c.x + x0 * c.y) * q_inv;
       }
@@ -438,8 +437,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
         c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
         c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], (int)c, true);
       }
-      qop[sub][w / 8][w % 8] = (int)c;
-      qlo[sub][w / 8][w % 8] = (int)lo;
+      qop[w / 8][w % 8] = (int)c;
+      qlo[w / 8][w % 8] = (int)lo;
     }
   }
 
@@ -459,39 +458,11 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   auto tref = [&](int it) {
     return tile_of(it_begin + it, t_count0, t_first0, t_first1, lo0, hi0, lo1, hi1);
   };
+  auto clamp_it = [&](int it) { return it < n_it ? it : n_it - 1; };
+  auto stage_of = [&](int it) { return smem + (it & (kStages - 1)) * SM::STAGE; };
 
-  v16f acc_o[kSub][NDT];
-#pragma unroll
-  for (int sub = 0; sub < kSub; ++sub)
-#pragma unroll
-    for (int d = 0; d < NDT; ++d) acc_o[sub][d] = v16f{};
-  float m_run[kSub], l_run[kSub];
-#pragma unroll
-  for (int sub = 0; sub < kSub; ++sub) {
-    m_run[sub] = -INFINITY;
-    l_run[sub] = 0.0f;
-  }
-
-  TileRegs regs;
-#pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (p < n_it) {
-      load_tile<D>(regs, tref(p), kc, vc, ks, vs, tid);
-      store_tile<D, MASK>(regs, tref(p), smem + p * SM::STAGE, kscale, cP, tid);
-    }
-  if (kStages - 1 < n_it) load_tile<D>(regs, tref(kStages - 1), kc, vc, ks, vs, tid);
-  __syncthreads();
-
-  int stage = 0;
-  for (int it = 0; it < n_it; ++it) {
-    const uint8_t* st = smem + stage * SM::STAGE;
-    const float* kf = (const float*)(st + SM::K_BYTES + SM::V_BYTES);
-    const float* wf = kf + 64;
-    const TileRef tr = tref(it);
-    const int base = tr.tile * 64;
-    const bool partial = MASK && (tr.lo > base || tr.hi < base + 64);
-
-    // K operands (shared by both sub-tiles)
+  // S^T = K . Q^T of the tile in stage st (raw integer-code products)
+  auto qk = [&](const uint8_t* st, v16f (&acc)[2]) {
     v8i kop[2][NSTEP];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
@@ -510,107 +481,136 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
                          (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
       }
     }
-    v16f acc_s[kSub][2];
+    acc[0] = v16f{};
+    acc[1] = v16f{};
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub)
+    for (int s = 0; s < NSTEP; ++s)
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        acc_s[sub][kh] = v16f{};
+      for (int kh = 0; kh < 2; ++kh) acc[kh] = mfma_fp8(kop[kh][s], qop[s], acc[kh]);
+    if constexpr (QLO)
 #pragma unroll
-        for (int s = 0; s < NSTEP; ++s) {
-          acc_s[sub][kh] = mfma_fp8(kop[kh][s], qop[sub][s], acc_s[sub][kh]);
-          if constexpr (QLO)
-            acc_s[sub][kh] = mfma_fp8_bscaled(kop[kh][s], qlo[sub][s], acc_s[sub][kh], 127 - kLoShift);
-        }
-      }
-
-    if (partial) {
-      // keys outside the segment: add -448 * 448 to their raw scores with one
-      // MFMA per key half (A: -448 at one k position of a masked key row,
-      // B: 448 at the same k position of every query column)
+      for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) acc[kh] = mfma_fp8_bscaled(kop[kh][s], qlo[s], acc[kh], 127 - kLoShift);
+  };
+  // keys of tile it outside its segment: add -448 * 448 to their raw scores
+  // with one MFMA per key half (A: -448 at one k position of a masked key row,
+  // B: 448 at the same k position of every query column)
+  auto mask_scores = [&](int it, v16f (&acc)[2]) {
+    const TileRef tr = tref(it);
+    const int base = tr.tile * 64;
+    if (tr.lo > base || tr.hi < base + 64) {
       const v8i ones = v8i{hh == 0 ? 0x7E : 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const int slot = base + 32 * kh + li;
         const bool masked = !(slot >= tr.lo && slot < tr.hi);
         const v8i bias = v8i{(hh == 0 && masked) ? 0xFE : 0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int sub = 0; sub < kSub; ++sub) acc_s[sub][kh] = mfma_fp8(bias, ones, acc_s[sub][kh]);
+        acc[kh] = mfma_fp8(bias, ones, acc[kh]);
       }
     }
-
-    // softmax of sub-tile 0 (overlaps the sub-tile 1 MFMAs), then its PV with
-    // the V operands that sub-tile 1 reuses
-    v8i plo;
-    v8i pop = softmax_tile<NDT, PLO>(acc_s[0], kf, wf, hh, m_run[0], l_run[0], acc_o[0], plo);
-    v8i vop[NDT];
+  };
+  // O^T += V^T . P'^T with the V tile in stage st
+  v16f acc_o[NDT];
+#pragma unroll
+  for (int d = 0; d < NDT; ++d) acc_o[d] = v16f{};
+  auto pv = [&](const uint8_t* st, const v8i& pop, const v8i& plo) {
 #pragma unroll
     for (int d = 0; d < NDT; ++d) {
       const uint8_t* vrow = st + SM::K_BYTES + (32 * d + li) * SM::VROW + 32 * hh;
       const uint4 v0 = *(const uint4*)(vrow);
       const uint4 v1 = *(const uint4*)(vrow + 16);
-      vop[d] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                   (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-      acc_o[0][d] = mfma_fp8(vop[d], pop, acc_o[0][d]);
-      if constexpr (PLO) acc_o[0][d] = mfma_fp8_bscaled(vop[d], plo, acc_o[0][d], 127 - kLoShift);
+      const v8i vop = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                          (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+      acc_o[d] = mfma_fp8(vop, pop, acc_o[d]);
+      if constexpr (PLO) acc_o[d] = mfma_fp8_bscaled(vop, plo, acc_o[d], 127 - kLoShift);
     }
-#pragma unroll
-    for (int sub = 1; sub < kSub; ++sub) {
-      pop = softmax_tile<NDT, PLO>(acc_s[sub], kf, wf, hh, m_run[sub], l_run[sub], acc_o[sub], plo);
-#pragma unroll
-      for (int d = 0; d < NDT; ++d) {
-        acc_o[sub][d] = mfma_fp8(vop[d], pop, acc_o[sub][d]);
-        if constexpr (PLO) acc_o[sub][d] = mfma_fp8_bscaled(vop[d], plo, acc_o[sub][d], 127 - kLoShift);
-      }
-    }
+  };
 
-    // staging of tile it + kStages - 1 (stored) and it + kStages (loaded), unconditional with
-    // the tile index clamped (past the end the copy lands in a stage nobody
-    // reads again), so that it shares a basic block with the PV products
-    const int nst = (stage + kStages - 1) % kStages;   // stage of tile it + kStages - 1
-    const int ts = it + kStages - 1 < n_it ? it + kStages - 1 : n_it - 1;
-    const int tl = it + kStages < n_it ? it + kStages : n_it - 1;
-    store_tile<D, MASK>(regs, tref(ts), smem + nst * SM::STAGE, kscale, cP, tid);
-    load_tile<D>(regs, tref(tl), kc, vc, ks, vs, tid);
-    __syncthreads();
-    stage = stage + 1 == kStages ? 0 : stage + 1;
+  // ---- prologue: tiles 0 and 1 staged, tile 2 in registers, and the V rows
+  // of the stage of tile -1 zeroed (the first iteration's product of the
+  // previous tile then adds nothing); scores of tile 0
+  TileRegs regs;
+  if (n_it > 0) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      load_tile<D>(regs, tref(clamp_it(p)), kc, vc, ks, vs, tid);
+      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale, cP, tid);
+    }
+    load_tile<D>(regs, tref(clamp_it(2)), kc, vc, ks, vs, tid);
   }
+  for (int i = tid; i < SM::V_BYTES / 16; i += kThreads)
+    ((uint4*)(stage_of(-1) + SM::K_BYTES))[i] = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  v16f acc_s[2];
+  qk(stage_of(0), acc_s);
+  if constexpr (MASK) mask_scores(0, acc_s);
+  v8i pop = v8i{}, plo = v8i{};
+
+  // ---- main loop: iteration it computes the softmax of tile it while the
+  // matrix cores take the PV product of tile it - 1 and the scores of tile
+  // it + 1; the ring holds tiles it - 1 .. it + 2
+  for (int it = 0; it < n_it; ++it) {
+    const float* kf = (const float*)(stage_of(it) + SM::K_BYTES + SM::V_BYTES);
+    const float* wf = kf + 64;
+    pv(stage_of(it - 1), pop, plo);
+    float t[32];
+    softmax_scores<NDT>(acc_s, kf, hh, m_run, l_run, acc_o, t);
+    // past the last tile these products read a stale stage and are unused
+    qk(stage_of(it + 1), acc_s);
+    if constexpr (MASK) mask_scores(it + 1, acc_s);
+    pop = softmax_probs<PLO>(t, wf, hh, l_run, plo);
+
+    // staging of tile it + 2 (stored into the stage tile it - 2 held) and it + 3
+    // (loaded), unconditional with the tile index clamped (past the end the
+    // copy lands in a stage nobody reads again)
+    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(it + 2), kscale, cP, tid);
+    load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, ks, vs, tid);
+#if RTV_ATTEND_SCHED > 0
+    // spread the score products of tile it + 1 over the exponentials
+#pragma unroll
+    for (int i = 0; i < 2 * NSTEP * (QLO ? 2 : 1); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, RTV_ATTEND_SCHED, 0);
+    }
+#endif
+    __syncthreads();
+  }
+  pv(stage_of(n_it - 1), pop, plo);
 
   // ---- epilogue ----------------------------------------------------------------
+  const float l_tot = xhalf_sum(l_run);
+  if (part >= 0) {
+    // partial result of a key range: O / c unnormalized, with (m, l)
+    const int q = wave * kQPW + li;
+    float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
+    const float inv_c = 1.0f / cP;
 #pragma unroll
-  for (int sub = 0; sub < kSub; ++sub) {
-    const int row = q_rows[sub];
-    const float l_tot = xhalf_sum(l_run[sub]);
-    if (part >= 0) {
-      // partial result of a key range: O / c unnormalized, with (m, l)
-      const int q = wave * kQPW + sub * 32 + li;
-      float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
-      const float inv_c = 1.0f / cP;
+    for (int d = 0; d < NDT; ++d)
 #pragma unroll
-      for (int d = 0; d < NDT; ++d)
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * d + 8 * g + 4 * hh;
+        *(float4*)(po + d0) = make_float4(acc_o[d][4 * g + 0] * inv_c, acc_o[d][4 * g + 1] * inv_c,
+                                          acc_o[d][4 * g + 2] * inv_c, acc_o[d][4 * g + 3] * inv_c);
+      }
+    if (hh == 0) *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) = make_float2(m_run, l_tot);
+    return;
+  }
+  const float scale = 1.0f / (cP * l_tot);
+  if (q_row < a.n_tokens) {
+    uint16_t* dst = a.out + (int64_t)q_row * a.ldo + (int64_t)head * D;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * d + 8 * g + 4 * hh;
-          *(float4*)(po + d0) = make_float4(acc_o[sub][d][4 * g + 0] * inv_c, acc_o[sub][d][4 * g + 1] * inv_c,
-                                            acc_o[sub][d][4 * g + 2] * inv_c, acc_o[sub][d][4 * g + 3] * inv_c);
-        }
-      if (hh == 0) *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) = make_float2(m_run[sub], l_tot);
-      continue;
-    }
-    const float scale = 1.0f / (cP * l_tot);
-    if (row < a.n_tokens) {
-      uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D;
+    for (int d = 0; d < NDT; ++d)
 #pragma unroll
-      for (int d = 0; d < NDT; ++d)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * d + 8 * g + 4 * hh;
-          uint2 w;
-          w.x = pack_bf16x2(acc_o[sub][d][4 * g + 0] * scale, acc_o[sub][d][4 * g + 1] * scale);
-          w.y = pack_bf16x2(acc_o[sub][d][4 * g + 2] * scale, acc_o[sub][d][4 * g + 3] * scale);
-          *(uint2*)(dst + d0) = w;
-        }
-    }
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * d + 8 * g + 4 * hh;
+        uint2 w;
+        w.x = pack_bf16x2(acc_o[d][4 * g + 0] * scale, acc_o[d][4 * g + 1] * scale);
+        w.y = pack_bf16x2(acc_o[d][4 * g + 2] * scale, acc_o[d][4 * g + 3] * scale);
+        *(uint2*)(dst + d0) = w;
+      }
   }
 }
 
