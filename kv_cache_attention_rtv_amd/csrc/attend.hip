@@ -16,19 +16,25 @@
 // barrier per tile; waves 0-3 stage the K rows and waves 4-7 the V rows of
 // tile t+2 while tile t is computed.
 //
-// Per wave, tile and sub-tile, with v_mfma_f32_32x32x64_f8f6f4 (e4m3, f32 acc):
-//   S^T[key][query] = K . Q^T            2 key halves x D/64 k-steps
+// Per wave and tile, with v_mfma_f32_32x32x64_f8f6f4 (e4m3, f32 accumulate):
+//   S^T[key][query] = K . Q^T + C_key     2 key halves x D/64 k-steps
 //   lane (hh, i) holds query i and 32 of the 64 keys: the softmax row is
 //   per lane plus one v_permlane32_swap with lane i^32;
-//   P' = p * w_key, w_key = sv_key * c, converted to e4m3, is the B operand of
-//   O^T[d][query] += V^T . P'^T          D/32 d sub-tiles.
+//   O^T[d][query] += V^T . P'^T           D/32 d sub-tiles
+//   L[r][query]   += U . P'^T             one product: the row sum
 // Scores: the queries of a workgroup share one e4m3 scale s_q, so the whole
-// per-score scale folds into a per-key factor kf = sk * s_q * log2(e)/sqrt(D)
-// and t - m = fma(S_raw, kf, -m) is one instruction.  The running max m is
-// lazy: it moves only when a tile's max exceeds it by more than kTau (log2
-// units), so p <= 2^kTau, and c = kPmax / (2^kTau * max sv over the window)
-// keeps P' below 448 with one constant for the whole window.
-// Output O = acc / (c * l), rounded to bf16.
+// per-score scale folds into a per-key factor kf = sk * s_q * log2(e)/sqrt(D).
+// P' carries the V scale of its key: P' = p * 55 * rho_key with
+// rho = sv / (max sv over the window), so that P' . Vcodes * max sv / 55 is
+// the weighted sum of V.  log2(55 rho) enters as the accumulator's initial
+// value C = log2(55 rho) / kf, so t = fma(S, kf, -m) = log2 P' and P' is
+// one exp2 and one conversion per score.  The row sum is taken from the
+// same e4m3 P' by the matrix cores, against U = 1/rho as two e4m3 terms
+// (rows 0 and 1 of U): numerator and denominator share the rounding of P',
+// and a key's weight no longer depends on the size of its V row.  The
+// running max m is lazy: it moves only when some P' would exceed kPmax, and
+// then leaves a factor 2^kTau of headroom.  Output O = acc * max sv / L,
+// rounded to bf16.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -41,9 +47,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 #ifndef RTV_ATTEND_WAVES
 #define RTV_ATTEND_WAVES 8
 #endif
-#ifndef RTV_ATTEND_SCHED
-#define RTV_ATTEND_SCHED 0
-#endif
 #ifndef RTV_ATTEND_WG_PER_CU
 #define RTV_ATTEND_WG_PER_CU 1
 #endif
@@ -54,6 +57,11 @@ constexpr int kQPB = kWaves * kQPW;         // queries per workgroup
 constexpr int kStages = 4;                  // LDS ring: tiles it - 1 .. it + 2
 constexpr float kTau = 3.0f;
 constexpr float kPmax = 440.0f;             // bound on P' (below the e4m3 max 448)
+constexpr float kLogPmax = 8.78135971f;     // log2(kPmax)
+constexpr float kPW = 55.0f;                // P' = p * kPW * rho, rho <= 1
+constexpr float kLogPW = 5.78135971f;       // log2(kPW)
+constexpr float kRhoMin = 0.0009765625f;    // 2^-10: floor of rho (U = 2^-2 / rho <= 256)
+constexpr float kKfMin = 7.8886091e-31f;    // 2^-100: floor of kf (zero K rows, zero queries)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaskFactor = 1e30f;        // kf of a key outside the window segment
 
@@ -65,6 +73,10 @@ __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f&
 // adds the low-order e4m3 part of a two-term operand
 __device__ __forceinline__ v16f mfma_fp8_bscaled(const v8i& a, const v8i& b, const v16f& c, int e) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, e);
+}
+// both operands scaled: A by 2^(ea - 127), B by 2^(eb - 127)
+__device__ __forceinline__ v16f mfma_fp8_scaled(const v8i& a, const v8i& b, const v16f& c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
 
 // two-term e4m3 of two values: hi = e4m3(x), lo = e4m3((x - hi) * 2^kLoShift)
@@ -101,17 +113,21 @@ struct Smem {
   static constexpr int KROW = D + 16;       // padded K row (bytes): conflict-free 16 B reads
   static constexpr int VROW = 64 + 16;      // padded transposed-V row
   static constexpr int K_BYTES = 64 * KROW;
-  static constexpr int V_BYTES = D * VROW;
-  static constexpr int STAGE = K_BYTES + V_BYTES + 2 * 64 * 4;   // + kf, wf
+  // V^T rows, then the two U rows and a zero row (zeroed once, never staged)
+  static constexpr int V_BYTES = (D + 3) * VROW;
+  static constexpr int U_OFF = K_BYTES + D * VROW;
+  static constexpr int KF_OFF = K_BYTES + V_BYTES;    // kf[64], then C[64]
+  static constexpr int STAGE = KF_OFF + 2 * 64 * 4;
 };
 
 // Staged tile: with 512 threads, threads 0..255 (waves 0-3) move the K rows
-// and kf, threads 256..511 (waves 4-7) the transposed V rows and wf; with
-// 256 threads every thread moves a K piece and a V piece.  D/4 bytes each.
+// and write kf and C, threads 256..511 (waves 4-7) move the transposed V rows
+// and write U; with 256 threads every thread does both.  D/4 bytes each, and
+// every thread holds both scales of key (thread & 63).
 constexpr int kStageJobs = kThreads >= 512 ? 1 : 2;
 struct TileRegs {
   uint4 c[kStageJobs][2];
-  float s[kStageJobs];
+  float sk, sv;
 };
 
 struct TileRef {
@@ -131,9 +147,9 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const u
     const uint8_t* src = (isv ? vc : kc) + (int64_t)t.tile * 64 * D + gt * LD_BYTES;
     r.c[j][0] = *(const uint4*)(src);
     if constexpr (LD_BYTES == 32) r.c[j][1] = *(const uint4*)(src + 16);
-    // every thread loads a scale (only 64 per job are used): no lane branch
-    r.s[j] = (isv ? vs : ks)[(int64_t)t.tile * 64 + (gt & 63)];
   }
+  r.sk = ks[(int64_t)t.tile * 64 + (gt & 63)];
+  r.sv = vs[(int64_t)t.tile * 64 + (gt & 63)];
 }
 
 // Byte offset in a stage of the 16-byte piece at byte b of a staged tile: K
@@ -172,22 +188,25 @@ __device__ __forceinline__ uint4 mask_v_piece(uint4 v, int b, int base, int lo, 
   return v;
 }
 
-// kscale = s_q * log2(e) / sqrt(D); wscale = c.  Branch-free apart from the
-// masking of partial tiles: K and V pieces differ only in their address, and
-// every thread writes the kf or wf entry of key (thread & 63); the threads
-// that share a key hold the same scale and write the same value.
+// byte position of key k in a transposed V (and U) row: the inverse of vt_key
+__device__ __forceinline__ int vt_pos(int k) {
+  return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);
+}
+
+// kscale = s_q * log2(e) / sqrt(D); inv_svmax = 1 / (max sv over the window).
+// The codes are stored branch-free apart from the masking of partial tiles:
+// K and V pieces differ only in their address.  The per-key factors of key
+// (thread & 63) are written by every thread of a side; threads that share a
+// key write the same values.
 template <int D, bool MASK>
 __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, uint8_t* st,
-                                           float kscale, float wscale, int tid) {
+                                           float kscale, float inv_svmax, int tid) {
   using SM = Smem<D>;
   constexpr int LD_BYTES = D / 4;
   const int gt = tid & 255;
   const int base = t.tile * 64;
   const bool partial = MASK && (t.lo > base || t.hi < base + 64);
   const int b = gt * LD_BYTES;
-  float* kf = (float*)(st + SM::K_BYTES + SM::V_BYTES);
-  const int key = gt & 63;
-  const bool ok = !MASK || (base + key >= t.lo && base + key < t.hi);
 #pragma unroll
   for (int j = 0; j < kStageJobs; ++j) {
     const bool isv = kStageJobs == 1 ? tid >= 256 : j == 1;
@@ -198,11 +217,33 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, 
       if (partial) q = isv ? mask_v_piece(q, bb, base, t.lo, t.hi) : mask_k_piece<D>(q, bb, base, t.lo, t.hi);
       *(uint4*)(st + (isv ? v_piece_at<D>(bb) : k_piece_at<D>(bb))) = q;
     }
-    // a key outside the segment gets kf = kMaskFactor: its raw score is the
-    // bias -448*448 added by the masking MFMA, so t ~ -2e35 and p = 0
-    const float kv = ok ? r.s[j] * kscale : kMaskFactor;
-    const float wv = ok ? r.s[j] * wscale : 0.0f;
-    kf[(isv ? 64 : 0) + key] = isv ? wv : kv;
+  }
+  const int key = gt & 63;
+  const bool ok = !MASK || (base + key >= t.lo && base + key < t.hi);
+  // rho of a zero V row is 1 (its codes are zero, and its score still counts
+  // in the row sum); tiny rows are floored so that U stays in range
+  const float rho = r.sv > 0.0f ? __builtin_fmaxf(r.sv * inv_svmax, kRhoMin) : 1.0f;
+  const bool kside = kStageJobs == 2 || __builtin_amdgcn_readfirstlane(tid) < 256;
+  const bool vside = kStageJobs == 2 || !kside;
+  if (kside) {
+    // a key outside the segment gets kf = kMaskFactor and C = 0: its raw score
+    // is the bias -448*448 added by the masking MFMA, so t ~ -2e35 and P' = 0
+    const float kf = __builtin_fmaxf(r.sk * kscale, kKfMin);
+    const float c = (kLogPW + __builtin_amdgcn_logf(rho)) * __builtin_amdgcn_rcpf(kf);
+    float* kfp = (float*)(st + SM::KF_OFF);
+    kfp[key] = ok ? kf : kMaskFactor;
+    kfp[64 + key] = ok ? c : 0.0f;
+  }
+  if (vside) {
+    // U = 2^-2 / rho in [2^-2, 2^8] as hi + lo e4m3 terms (scaled back by 2^2
+    // in the row-sum product)
+    const float u = 0.25f * __builtin_amdgcn_rcpf(rho);
+    const int hi = __builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false);
+    const float uh = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false)[0];
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(u - uh, 0.0f, 0, false);
+    uint8_t* urow = st + SM::U_OFF + vt_pos(key);
+    urow[0] = (uint8_t)hi;
+    urow[SM::VROW] = (uint8_t)lo;
   }
 }
 
@@ -231,72 +272,57 @@ __device__ __forceinline__ void scores(const v16f (&s)[2], const float* kf, int 
     }
 }
 
-// Softmax of one 32-query tile over one 64-key tile, first half: t = score - m
-// for the lane's 32 keys, with the lazy running-max update (rare: rescales l
-// and the O accumulator).
+// Softmax of one 32-query tile over one 64-key tile, first half (after
+// t = fma(S, kf, -m), mx = the tile max of t): the lazy running-max update.
+// Rare: only when some P' would exceed kPmax (always on the first tile, where
+// m = -inf makes every t = +inf); it rescales the O and row-sum
+// accumulators and leaves the largest P' of the tile at kPmax / 2^kTau.
 template <int NDT>
-__device__ __forceinline__ void softmax_scores(const v16f (&s)[2], const float* kf, int hh, float& m,
-                                               float& l, v16f (&o)[NDT], float (&t)[32]) {
-  scores(s, kf, hh, m, t);
-  float mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 32; j += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(t[j], t[j + 1]));
-  mx = xhalf_max(mx);
-  // lazy rescale: only when the tile max exceeds the reference by > kTau
-  // (always on the first tile, where m = -inf makes every t = +inf)
-  if (__builtin_expect(__any(mx > kTau), 0)) {
-    scores(s, kf, hh, 0.0f, t);   // raw scaled scores
+__device__ __forceinline__ void lazy_rescale(const v16f (&s)[2], const float* kf, int hh, float mx,
+                                             float& m, v16f (&o)[NDT], v16f& lsum, float (&t)[32]) {
+  if (__builtin_expect(__any(mx > kLogPmax), 0)) {
+    scores(s, kf, hh, 0.0f, t);   // raw log2 P' before the shift by m
     float raw = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 32; ++j) raw = __builtin_fmaxf(raw, t[j]);
     raw = xhalf_max(raw);
-    const float m_new = __builtin_fmaxf(m, raw);
+    const float m_new = __builtin_fmaxf(m, raw - (kLogPmax - kTau));
     const float alpha = exp2f(m - m_new);           // 0 on the first tile (m = -inf)
-    l *= alpha;
 #pragma unroll
     for (int d = 0; d < NDT; ++d) o[d] *= alpha;
+    lsum *= alpha;
 #pragma unroll
     for (int j = 0; j < 32; ++j) t[j] -= m_new;
     m = m_new;
   }
 }
 
-// Second half: p = 2^t, l += p, and the e4m3 P' = p * w_key, the B operand of
-// the PV product (PRECISE: as two terms).
+// Second half, in quarters (keys 8c .. 8c + 7 of the lane): P' = 2^t in e4m3,
+// the B operand of the PV and row-sum products (PRECISE: as two terms).
 template <bool PRECISE>
-__device__ __forceinline__ v8i softmax_probs(const float (&t)[32], const float* wf, int hh, float& l,
-                                             v8i& plo) {
-  v8i pop;
-  uint32_t prev = 0;
+__device__ __forceinline__ void probs_quarter(int c, const float (&t)[32], v8i& pop, v8i& plo) {
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
+  for (int w = 2 * c; w < 2 * c + 2; ++w) {
+    float pp[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int key0 = 32 * kh + 8 * g + 4 * hh;
-      const float4 w4 = *(const float4*)(wf + key0);
-      const float ww[4] = {w4.x, w4.y, w4.z, w4.w};
-      float pp[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(t[16 * kh + 4 * g + e]);
-        l += p;
-        pp[e] = p * ww[e];
-      }
-      if constexpr (PRECISE) {
-        uint32_t c = 0, lo = 0;
-        split_fp8x2<false>(pp[0], pp[1], c, lo);
-        split_fp8x2<true>(pp[2], pp[3], c, lo);
-        pop[4 * kh + g] = (int)c;
-        plo[4 * kh + g] = (int)lo;
-      } else {
-        uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], (int)prev, false);
-        c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], (int)c, true);
-        pop[4 * kh + g] = (int)c;
-        prev = c;
-      }
+    for (int e = 0; e < 4; ++e) pp[e] = __builtin_amdgcn_exp2f(t[4 * w + e]);
+    if constexpr (PRECISE) {
+      uint32_t hi = 0, lo = 0;
+      split_fp8x2<false>(pp[0], pp[1], hi, lo);
+      split_fp8x2<true>(pp[2], pp[3], hi, lo);
+      pop[w] = (int)hi;
+      plo[w] = (int)lo;
+    } else {
+      uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], 0, false);
+      hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], (int)hi, true);
+      pop[w] = (int)hi;
     }
-  return pop;
+  }
 }
+
+// scheduling fence between the interleaved chunks of matrix-core and vector
+// work: LDS reads, scalar and global-read instructions may still move across
+__device__ __forceinline__ void chunk_fence() { __builtin_amdgcn_sched_barrier(0x0124); }
 
 // MASK = false: every segment boundary of the window falls on a 64-slot tile
 // boundary (the host checks), so no tile needs masking and the kernel carries
@@ -396,7 +422,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   }
   const float q_inv = qamax > 0.0f ? kFp8Max / qamax : 0.0f;
   const float kscale = (qamax / kFp8Max) * (kLog2e / sqrtf((float)D));
-  const float cP = svmax > 0.0f ? kPmax / (exp2f(kTau) * svmax) : 1.0f;
+  const float inv_svmax = svmax > 0.0f ? 1.0f / svmax : 0.0f;
 
   // ---- Q prologue pass 2: e4m3 codes in the B-operand layout ---------------
   // operand step s, byte b <-> d: D=128: d = 64 s + 32 hh + b; D=64: byte b < 16
@@ -461,9 +487,10 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   auto clamp_it = [&](int it) { return it < n_it ? it : n_it - 1; };
   auto stage_of = [&](int it) { return smem + (it & (kStages - 1)) * SM::STAGE; };
 
-  // S^T = K . Q^T of the tile in stage st (raw integer-code products)
-  auto qk = [&](const uint8_t* st, v16f (&acc)[2]) {
-    v8i kop[2][NSTEP];
+  // S^T = K . Q^T + C of the tile in stage st: K operands, the accumulator
+  // initial value C of the lane's 32 keys, and product j (key half j % 2,
+  // k-step j / 2) of the 2 * NSTEP
+  auto load_k = [&](const uint8_t* st, v8i (&kop)[2][NSTEP], v16f (&acc)[2]) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       const uint8_t* krow = st + (32 * kh + li) * SM::KROW;
@@ -481,17 +508,22 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
                          (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
       }
     }
-    acc[0] = v16f{};
-    acc[1] = v16f{};
+    const float* cp = (const float*)(st + SM::KF_OFF) + 64;
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s)
+    for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) acc[kh] = mfma_fp8(kop[kh][s], qop[s], acc[kh]);
-    if constexpr (QLO)
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) acc[kh] = mfma_fp8_bscaled(kop[kh][s], qlo[s], acc[kh], 127 - kLoShift);
+      for (int g = 0; g < 4; ++g) {
+        const float4 c4 = *(const float4*)(cp + 32 * kh + 8 * g + 4 * hh);
+        acc[kh][4 * g + 0] = c4.x;
+        acc[kh][4 * g + 1] = c4.y;
+        acc[kh][4 * g + 2] = c4.z;
+        acc[kh][4 * g + 3] = c4.w;
+      }
+  };
+  auto qk_step = [&](int j, const v8i (&kop)[2][NSTEP], v16f (&acc)[2]) {
+    const int kh = j & 1, s = j >> 1;
+    acc[kh] = mfma_fp8(kop[kh][s], qop[s], acc[kh]);
+    if constexpr (QLO) acc[kh] = mfma_fp8_bscaled(kop[kh][s], qlo[s], acc[kh], 127 - kLoShift);
   };
   // keys of tile it outside its segment: add -448 * 448 to their raw scores
   // with one MFMA per key half (A: -448 at one k position of a masked key row,
@@ -510,42 +542,63 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
       }
     }
   };
-  // O^T += V^T . P'^T with the V tile in stage st
+  // O^T += V^T . P'^T with the V tile in stage st, and the row sum
+  // L += U . P'^T: lanes of rows 0 and 1 read the U rows of the stage, the
+  // others a zero row
   v16f acc_o[NDT];
 #pragma unroll
   for (int d = 0; d < NDT; ++d) acc_o[d] = v16f{};
-  auto pv = [&](const uint8_t* st, const v8i& pop, const v8i& plo) {
+  v16f acc_l = v16f{};
+  const int u_off = SM::U_OFF + (li < 2 ? li : 2) * SM::VROW + 32 * hh;
+  auto load_v = [&](const uint8_t* st, v8i (&vop)[NDT + 1]) {
 #pragma unroll
-    for (int d = 0; d < NDT; ++d) {
-      const uint8_t* vrow = st + SM::K_BYTES + (32 * d + li) * SM::VROW + 32 * hh;
+    for (int d = 0; d <= NDT; ++d) {
+      const uint8_t* vrow = d < NDT ? st + SM::K_BYTES + (32 * d + li) * SM::VROW + 32 * hh : st + u_off;
       const uint4 v0 = *(const uint4*)(vrow);
       const uint4 v1 = *(const uint4*)(vrow + 16);
-      const v8i vop = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                          (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-      acc_o[d] = mfma_fp8(vop, pop, acc_o[d]);
-      if constexpr (PLO) acc_o[d] = mfma_fp8_bscaled(vop, plo, acc_o[d], 127 - kLoShift);
+      vop[d] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                   (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+    }
+  };
+  // product j of the NDT + 1: d sub-tile j, or the row sum (j = NDT)
+  auto pv_step = [&](int j, const v8i (&vop)[NDT + 1], const v8i& pop, const v8i& plo) {
+    if (j < NDT) {
+      acc_o[j] = mfma_fp8(vop[j], pop, acc_o[j]);
+      if constexpr (PLO) acc_o[j] = mfma_fp8_bscaled(vop[j], plo, acc_o[j], 127 - kLoShift);
+    } else {
+      acc_l = mfma_fp8_scaled(vop[NDT], pop, acc_l, 127 + 2, 127);
+      if constexpr (PLO) acc_l = mfma_fp8_scaled(vop[NDT], plo, acc_l, 127 + 2, 127 - kLoShift);
     }
   };
 
-  // ---- prologue: tiles 0 and 1 staged, tile 2 in registers, and the V rows
-  // of the stage of tile -1 zeroed (the first iteration's product of the
-  // previous tile then adds nothing); scores of tile 0
+  // ---- prologue: tiles 0 and 1 staged, tile 2 in registers, the V and U
+  // rows of the stage of tile -1 zeroed (the first iteration's products of the
+  // previous tile then add nothing), the zero rows of the other stages; scores
+  // of tile 0
   TileRegs regs;
   if (n_it > 0) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       load_tile<D>(regs, tref(clamp_it(p)), kc, vc, ks, vs, tid);
-      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale, cP, tid);
+      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale, inv_svmax, tid);
     }
     load_tile<D>(regs, tref(clamp_it(2)), kc, vc, ks, vs, tid);
   }
   for (int i = tid; i < SM::V_BYTES / 16; i += kThreads)
     ((uint4*)(stage_of(-1) + SM::K_BYTES))[i] = make_uint4(0, 0, 0, 0);
+  if (tid < (kStages - 1) * (SM::VROW / 16))
+    ((uint4*)(smem + (tid / (SM::VROW / 16)) * SM::STAGE + SM::U_OFF + 2 * SM::VROW))[tid % (SM::VROW / 16)] =
+        make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY;
   v16f acc_s[2];
-  qk(stage_of(0), acc_s);
+  {
+    v8i kop[2][NSTEP];
+    load_k(stage_of(0), kop, acc_s);
+#pragma unroll
+    for (int j = 0; j < 2 * NSTEP; ++j) qk_step(j, kop, acc_s);
+  }
   if constexpr (MASK) mask_scores(0, acc_s);
   v8i pop = v8i{}, plo = v8i{};
 
@@ -553,40 +606,76 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   // matrix cores take the PV product of tile it - 1 and the scores of tile
   // it + 1; the ring holds tiles it - 1 .. it + 2
   for (int it = 0; it < n_it; ++it) {
-    const float* kf = (const float*)(stage_of(it) + SM::K_BYTES + SM::V_BYTES);
-    const float* wf = kf + 64;
-    pv(stage_of(it - 1), pop, plo);
+    // (1) the PV and row-sum products of tile it - 1, interleaved with the
+    // scores of tile it: t = fma(S, kf, -m), a quarter (8 keys) per product
+    const float* kf = (const float*)(stage_of(it) + SM::KF_OFF);
+    float4 kf4[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) kf4[w] = *(const float4*)(kf + 32 * (w >> 2) + 8 * (w & 3) + 4 * hh);
+    v8i vop[NDT + 1];
+    load_v(stage_of(it - 1), vop);
     float t[32];
-    softmax_scores<NDT>(acc_s, kf, hh, m_run, l_run, acc_o, t);
-    // past the last tile these products read a stale stage and are unused
-    qk(stage_of(it + 1), acc_s);
+#pragma unroll
+    for (int c = 0; c < 4 || c <= NDT; ++c) {
+      if (c <= NDT) pv_step(c, vop, pop, plo);
+      if (c < 4) {
+#pragma unroll
+        for (int w = 2 * c; w < 2 * c + 2; ++w) {
+          const float kk[4] = {kf4[w].x, kf4[w].y, kf4[w].z, kf4[w].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[4 * w + e] = __builtin_fmaf(acc_s[w >> 2][4 * (w & 3) + e], kk[e], -m_run);
+        }
+      }
+      chunk_fence();
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 32; j += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(t[j], t[j + 1]));
+    mx = xhalf_max(mx);
+    lazy_rescale<NDT>(acc_s, kf, hh, mx, m_run, acc_o, acc_l, t);
+
+    // (2) the score products of tile it + 1 (past the last tile they read a
+    // stale stage and are unused), interleaved with P' of tile it
+    {
+      v8i kop[2][NSTEP];
+      load_k(stage_of(it + 1), kop, acc_s);
+#pragma unroll
+      for (int c = 0; c < 4 || c < 2 * NSTEP; ++c) {
+        if (c < 2 * NSTEP) qk_step(c, kop, acc_s);
+        if (c < 4) probs_quarter<PLO>(c, t, pop, plo);
+        chunk_fence();
+      }
+    }
+    // keep the exponentials here rather than sunk past the staging branches
+    // towards their use in the next iteration
+    asm volatile("" ::"v"(pop));
+    if constexpr (PLO) asm volatile("" ::"v"(plo));
     if constexpr (MASK) mask_scores(it + 1, acc_s);
-    pop = softmax_probs<PLO>(t, wf, hh, l_run, plo);
 
     // staging of tile it + 2 (stored into the stage tile it - 2 held) and it + 3
     // (loaded), unconditional with the tile index clamped (past the end the
     // copy lands in a stage nobody reads again)
-    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(it + 2), kscale, cP, tid);
+    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(it + 2), kscale, inv_svmax, tid);
     load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, ks, vs, tid);
-#if RTV_ATTEND_SCHED > 0
-    // spread the score products of tile it + 1 over the exponentials
-#pragma unroll
-    for (int i = 0; i < 2 * NSTEP * (QLO ? 2 : 1); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, RTV_ATTEND_SCHED, 0);
-    }
-#endif
     __syncthreads();
   }
-  pv(stage_of(n_it - 1), pop, plo);
+  {
+    v8i vop[NDT + 1];
+    load_v(stage_of(n_it - 1), vop);
+#pragma unroll
+    for (int j = 0; j <= NDT; ++j) pv_step(j, vop, pop, plo);
+  }
 
   // ---- epilogue ----------------------------------------------------------------
-  const float l_tot = xhalf_sum(l_run);
+  // row sum: rows 0 and 1 of L (registers 0 and 1 of the lanes hh = 0; the
+  // same registers of the lanes hh = 1 hold the zero rows 4 and 5)
+  const float l_tot = xhalf_sum(acc_l[0] + acc_l[1]);
   if (part >= 0) {
-    // partial result of a key range: O / c unnormalized, with (m, l)
+    // partial result of a key range: sum p V and sum p (p = 2^(score - m)),
+    // with m
     const int q = wave * kQPW + li;
     float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
-    const float inv_c = 1.0f / cP;
+    const float inv_c = svmax / kPW;
 #pragma unroll
     for (int d = 0; d < NDT; ++d)
 #pragma unroll
@@ -595,10 +684,10 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
         *(float4*)(po + d0) = make_float4(acc_o[d][4 * g + 0] * inv_c, acc_o[d][4 * g + 1] * inv_c,
                                           acc_o[d][4 * g + 2] * inv_c, acc_o[d][4 * g + 3] * inv_c);
       }
-    if (hh == 0) *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) = make_float2(m_run, l_tot);
+    if (hh == 0) *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) = make_float2(m_run, l_tot / kPW);
     return;
   }
-  const float scale = 1.0f / (cP * l_tot);
+  const float scale = svmax / l_tot;
   if (q_row < a.n_tokens) {
     uint16_t* dst = a.out + (int64_t)q_row * a.ldo + (int64_t)head * D;
 #pragma unroll
