@@ -272,6 +272,19 @@ __device__ __forceinline__ void scores(const v16f (&s)[2], const float* kf, int 
     }
 }
 
+// max of 32 values as a tree of three-input maxima (16 instructions)
+__device__ __forceinline__ float max32(const float (&t)[32]) {
+  float a[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) a[i] = __builtin_fmaxf(__builtin_fmaxf(t[3 * i], t[3 * i + 1]), t[3 * i + 2]);
+  a[10] = __builtin_fmaxf(t[30], t[31]);
+  const float b0 = __builtin_fmaxf(__builtin_fmaxf(a[0], a[1]), a[2]);
+  const float b1 = __builtin_fmaxf(__builtin_fmaxf(a[3], a[4]), a[5]);
+  const float b2 = __builtin_fmaxf(__builtin_fmaxf(a[6], a[7]), a[8]);
+  const float b3 = __builtin_fmaxf(a[9], a[10]);
+  return __builtin_fmaxf(__builtin_fmaxf(b0, b1), __builtin_fmaxf(b2, b3));
+}
+
 // Softmax of one 32-query tile over one 64-key tile, first half (after
 // t = fma(S, kf, -m), mx = the tile max of t): the lazy running-max update.
 // Rare: only when some P' would exceed kPmax (always on the first tile, where
@@ -313,7 +326,10 @@ __device__ __forceinline__ void probs_quarter(int c, const float (&t)[32], v8i& 
       pop[w] = (int)hi;
       plo[w] = (int)lo;
     } else {
-      uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], 0, false);
+      // the low half is written first and the high half next, so the old
+      // contents of the register do not matter: pp[0], dead after this
+      // instruction, is that register
+      uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], __float_as_int(pp[0]), false);
       hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], (int)hi, true);
       pop[w] = (int)hi;
     }
@@ -606,6 +622,14 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   // matrix cores take the PV product of tile it - 1 and the scores of tile
   // it + 1; the ring holds tiles it - 1 .. it + 2
   for (int it = 0; it < n_it; ++it) {
+    // (0) staging of tile it + 2 into the stage that tile it - 2 held (last
+    // read before the previous barrier; first read of tile it + 2 after the
+    // next one) and the loads of tile it + 3; at the top of the iteration so
+    // that its latency overlaps the products.  Unconditional with the tile
+    // index clamped: past the end the copy lands in a stage nobody reads again
+    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(it + 2), kscale, inv_svmax, tid);
+    load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, ks, vs, tid);
+
     // (1) the PV and row-sum products of tile it - 1, interleaved with the
     // scores of tile it: t = fma(S, kf, -m), a quarter (8 keys) per product
     const float* kf = (const float*)(stage_of(it) + SM::KF_OFF);
@@ -628,10 +652,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
       }
       chunk_fence();
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 32; j += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(t[j], t[j + 1]));
-    mx = xhalf_max(mx);
+    const float mx = xhalf_max(max32(t));
     lazy_rescale<NDT>(acc_s, kf, hh, mx, m_run, acc_o, acc_l, t);
 
     // (2) the score products of tile it + 1 (past the last tile they read a
@@ -652,11 +673,6 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     if constexpr (PLO) asm volatile("" ::"v"(plo));
     if constexpr (MASK) mask_scores(it + 1, acc_s);
 
-    // staging of tile it + 2 (stored into the stage tile it - 2 held) and it + 3
-    // (loaded), unconditional with the tile index clamped (past the end the
-    // copy lands in a stage nobody reads again)
-    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(it + 2), kscale, inv_svmax, tid);
-    load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, ks, vs, tid);
     __syncthreads();
   }
   {
