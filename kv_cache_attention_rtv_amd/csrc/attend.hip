@@ -32,7 +32,7 @@
 // same e4m3 P' by the matrix cores, against U = 1/rho as two e4m3 terms
 // (rows 0 and 1 of U): numerator and denominator share the rounding of P',
 // and a key's weight no longer depends on the size of its V row.  The
-// running max m is lazy: it moves only when some P' would exceed kPmax, and
+// running max m is lazy: it moves only when some P' would exceed 440, and
 // then leaves a factor 2^kTau of headroom.  Output O = acc * max sv / L,
 // rounded to bf16.
 #include "device_common.hpp"
@@ -56,12 +56,12 @@ constexpr int kQPW = 32;                    // queries per wave
 constexpr int kQPB = kWaves * kQPW;         // queries per workgroup
 constexpr int kStages = 4;                  // LDS ring: tiles it - 1 .. it + 2
 constexpr float kTau = 3.0f;
-constexpr float kPmax = 440.0f;             // bound on P' (below the e4m3 max 448)
-constexpr float kLogPmax = 8.78135971f;     // log2(kPmax)
+constexpr float kLogPmax = 8.78135971f;     // log2(440): bound on P' (below the e4m3 max 448)
 constexpr float kPW = 55.0f;                // P' = p * kPW * rho, rho <= 1
 constexpr float kLogPW = 5.78135971f;       // log2(kPW)
 constexpr float kRhoMin = 0.0009765625f;    // 2^-10: floor of rho (U = 2^-2 / rho <= 256)
-constexpr float kKfMin = 7.8886091e-31f;    // 2^-100: floor of kf (zero K rows, zero queries)
+constexpr float kScaleMin = 8.6736174e-19f; // 2^-60: floor of sk and of the query scale factor,
+                                            // so that kf >= 2^-120 and C stays finite
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaskFactor = 1e30f;        // kf of a key outside the window segment
 
@@ -122,12 +122,14 @@ struct Smem {
 
 // Staged tile: with 512 threads, threads 0..255 (waves 0-3) move the K rows
 // and write kf and C, threads 256..511 (waves 4-7) move the transposed V rows
-// and write U; with 256 threads every thread does both.  D/4 bytes each, and
-// every thread holds both scales of key (thread & 63).
+// and the U rows; with 256 threads every thread does both.  D/4 bytes of codes
+// each, and every thread holds the factors of key (thread & 63).
 constexpr int kStageJobs = kThreads >= 512 ? 1 : 2;
 struct TileRegs {
   uint4 c[kStageJobs][2];
-  float sk, sv;
+  // K side: the factor record (max(sk, kScaleMin), log2(55 rho) / that, 0, 0)
+  // of key (thread & 63); V side: 16-byte piece (thread & 7) of the U rows
+  uint4 x[kStageJobs];
 };
 
 struct TileRef {
@@ -137,7 +139,7 @@ struct TileRef {
 
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const uint8_t* kc,
-                                          const uint8_t* vc, const float* ks, const float* vs,
+                                          const uint8_t* vc, const uint4* frec, const uint4* fu,
                                           int tid) {
   constexpr int LD_BYTES = D / 4;
   const int gt = tid & 255;
@@ -147,9 +149,8 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const u
     const uint8_t* src = (isv ? vc : kc) + (int64_t)t.tile * 64 * D + gt * LD_BYTES;
     r.c[j][0] = *(const uint4*)(src);
     if constexpr (LD_BYTES == 32) r.c[j][1] = *(const uint4*)(src + 16);
+    r.x[j] = isv ? fu[(int64_t)t.tile * 8 + (gt & 7)] : frec[(int64_t)t.tile * 64 + (gt & 63)];
   }
-  r.sk = ks[(int64_t)t.tile * 64 + (gt & 63)];
-  r.sv = vs[(int64_t)t.tile * 64 + (gt & 63)];
 }
 
 // Byte offset in a stage of the 16-byte piece at byte b of a staged tile: K
@@ -193,14 +194,14 @@ __device__ __forceinline__ int vt_pos(int k) {
   return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);
 }
 
-// kscale = s_q * log2(e) / sqrt(D); inv_svmax = 1 / (max sv over the window).
+// kscale = max(s_q * log2(e) / sqrt(D), kScaleMin), inv_kscale = 1 / kscale.
 // The codes are stored branch-free apart from the masking of partial tiles:
-// K and V pieces differ only in their address.  The per-key factors of key
-// (thread & 63) are written by every thread of a side; threads that share a
-// key write the same values.
+// K and V pieces differ only in their address.  The K side writes kf and C of
+// key (thread & 63), the V side the U rows; threads that share a key or a
+// piece write the same values.
 template <int D, bool MASK>
 __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, uint8_t* st,
-                                           float kscale, float inv_svmax, int tid) {
+                                           float kscale, float inv_kscale, int tid) {
   using SM = Smem<D>;
   constexpr int LD_BYTES = D / 4;
   const int gt = tid & 255;
@@ -218,32 +219,77 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, 
       *(uint4*)(st + (isv ? v_piece_at<D>(bb) : k_piece_at<D>(bb))) = q;
     }
   }
-  const int key = gt & 63;
-  const bool ok = !MASK || (base + key >= t.lo && base + key < t.hi);
-  // rho of a zero V row is 1 (its codes are zero, and its score still counts
-  // in the row sum); tiny rows are floored so that U stays in range
-  const float rho = r.sv > 0.0f ? __builtin_fmaxf(r.sv * inv_svmax, kRhoMin) : 1.0f;
   const bool kside = kStageJobs == 2 || __builtin_amdgcn_readfirstlane(tid) < 256;
   const bool vside = kStageJobs == 2 || !kside;
+  const uint4 xk = r.x[0];
+  const uint4 xv = r.x[kStageJobs - 1];
   if (kside) {
-    // a key outside the segment gets kf = kMaskFactor and C = 0: its raw score
-    // is the bias -448*448 added by the masking MFMA, so t ~ -2e35 and P' = 0
-    const float kf = __builtin_fmaxf(r.sk * kscale, kKfMin);
-    const float c = (kLogPW + __builtin_amdgcn_logf(rho)) * __builtin_amdgcn_rcpf(kf);
+    // t = (S + C) * kf - m = S * kf + log2(55 rho) - m.  A key outside the
+    // segment gets kf = kMaskFactor and C = 0: its raw score is the bias
+    // -448*448 added by the masking MFMA, so t ~ -2e35 and P' = 0
+    const int key = gt & 63;
+    const bool ok = !MASK || (base + key >= t.lo && base + key < t.hi);
+    const float kf = __uint_as_float(xk.x) * kscale;
+    const float c = __uint_as_float(xk.y) * inv_kscale;
     float* kfp = (float*)(st + SM::KF_OFF);
     kfp[key] = ok ? kf : kMaskFactor;
     kfp[64 + key] = ok ? c : 0.0f;
   }
   if (vside) {
-    // U = 2^-2 / rho in [2^-2, 2^8] as hi + lo e4m3 terms (scaled back by 2^2
-    // in the row-sum product)
-    const float u = 0.25f * __builtin_amdgcn_rcpf(rho);
-    const int hi = __builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false);
-    const float uh = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false)[0];
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(u - uh, 0.0f, 0, false);
-    uint8_t* urow = st + SM::U_OFF + vt_pos(key);
-    urow[0] = (uint8_t)hi;
-    urow[SM::VROW] = (uint8_t)lo;
+    const int piece = gt & 7;
+    *(uint4*)(st + SM::U_OFF + (piece >> 2) * SM::VROW + 16 * (piece & 3)) = xv;
+  }
+}
+
+// Per-window key factors, one workgroup per (KV head, part of the window's
+// tiles); every workgroup first takes the window's max V scale svmax.  For
+// each slot of a window tile: rho = sv / svmax (1 for a zero V row, at least
+// kRhoMin), the record (sk' = max(sk, kScaleMin), log2(55 rho) / sk', 0, 0),
+// and the two e4m3 terms of 2^-2 / rho at the slot's byte position in the U
+// rows.  Slots of a partial
+// tile outside the window get factors too (from whatever their scales hold);
+// the attention masks them.
+constexpr int kFactorParts = 8;
+__global__ __launch_bounds__(256) void factors_kernel(AttendArgs a) {
+  __shared__ float red[4];
+  const int h = blockIdx.x / kFactorParts;
+  const int part = blockIdx.x % kFactorParts;
+  const int tid = threadIdx.x;
+  const int64_t Sp = a.slots_padded;
+  const float* ks = a.ks + (int64_t)h * Sp;
+  const float* vs = a.vs + (int64_t)h * Sp;
+  float svmax = 0.0f;
+  for (int s = 0; s < a.n_segments; ++s)
+    for (int64_t slot = a.seg_lo[s] + tid; slot < a.seg_hi[s]; slot += 256)
+      svmax = __builtin_fmaxf(svmax, vs[slot]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) svmax = __builtin_fmaxf(svmax, __shfl_xor(svmax, o));
+  if ((tid & 63) == 0) red[tid >> 6] = svmax;
+  __syncthreads();
+  svmax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  if (part == 0 && tid == 0) a.fac_sv[h] = svmax;
+  const float inv = svmax > 0.0f ? 1.0f / svmax : 0.0f;
+
+  float4* rec = (float4*)a.fac_l + (int64_t)h * a.ring_tiles * 64;
+  uint8_t* fu = a.fac_u + (int64_t)h * a.ring_tiles * 128;
+  const int key = tid & 63;
+  for (int s = 0; s < a.n_segments; ++s) {
+    if (a.seg_hi[s] <= a.seg_lo[s]) continue;
+    const int t0 = (int)(a.seg_lo[s] / 64), t1 = (int)((a.seg_hi[s] - 1) / 64);
+    for (int tile = t0 + part * 4 + (tid >> 6); tile <= t1; tile += kFactorParts * 4) {
+      const int64_t slot = (int64_t)tile * 64 + key;
+      const float sv = vs[slot];
+      const float sk = ks[slot];
+      const float rho = sv > 0.0f ? __builtin_fmaxf(sv * inv, kRhoMin) : 1.0f;
+      const float skf = __builtin_fmaxf(sk, kScaleMin);
+      rec[slot] = make_float4(skf, (kLogPW + __builtin_amdgcn_logf(rho)) / skf, 0.0f, 0.0f);
+      const float u = 0.25f / rho;
+      const int hi = __builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false);
+      const float uh = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false)[0];
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(u - uh, 0.0f, 0, false);
+      fu[(int64_t)tile * 128 + vt_pos(key)] = (uint8_t)hi;
+      fu[(int64_t)tile * 128 + 64 + vt_pos(key)] = (uint8_t)lo;
+    }
   }
 }
 
@@ -287,9 +333,9 @@ __device__ __forceinline__ float max32(const float (&t)[32]) {
 
 // Softmax of one 32-query tile over one 64-key tile, first half (after
 // t = fma(S, kf, -m), mx = the tile max of t): the lazy running-max update.
-// Rare: only when some P' would exceed kPmax (always on the first tile, where
+// Rare: only when some P' would exceed 440 (always on the first tile, where
 // m = -inf makes every t = +inf); it rescales the O and row-sum
-// accumulators and leaves the largest P' of the tile at kPmax / 2^kTau.
+// accumulators and leaves the largest P' of the tile at 440 / 2^kTau.
 template <int NDT>
 __device__ __forceinline__ void lazy_rescale(const v16f (&s)[2], const float* kf, int hh, float mx,
                                              float& m, v16f (&o)[NDT], v16f& lsum, float (&t)[32]) {
@@ -358,7 +404,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   constexpr int NDT = D / 32;               // 32-row d sub-tiles of O^T
   constexpr int P = D / 4;                  // RoPE pairs per lane
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * SM::STAGE];
-  __shared__ float red[2 * kWaves];
+  __shared__ float red[kWaves];
 
   // work item: a whole unit (query tile x head) or one key-range part of one
   const int xcd = blockIdx.x & 7;
@@ -386,16 +432,9 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   const int64_t Sp = a.slots_padded;
   const uint8_t* kc = a.kc + (int64_t)kvh * Sp * D;
   const uint8_t* vc = a.vc + (int64_t)kvh * Sp * D;
-  const float* ks = a.ks + (int64_t)kvh * Sp;
-  const float* vs = a.vs + (int64_t)kvh * Sp;
-
-  // ---- window-wide max of the V scales -> P' scale constant c -------------
-  float svmax = 0.0f;
-  for (int64_t slot = a.seg_lo[0] + tid; slot < a.seg_hi[0]; slot += kThreads)
-    svmax = __builtin_fmaxf(svmax, vs[slot]);
-  if (a.n_segments > 1)
-    for (int64_t slot = a.seg_lo[1] + tid; slot < a.seg_hi[1]; slot += kThreads)
-      svmax = __builtin_fmaxf(svmax, vs[slot]);
+  const uint4* frec = (const uint4*)a.fac_l + (int64_t)kvh * a.ring_tiles * 64;
+  const uint4* fu = (const uint4*)(a.fac_u + (int64_t)kvh * a.ring_tiles * 128);
+  const float svmax = a.fac_sv[kvh];   // window max of the V scales
 
   // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
   const int q_row = qtile * kQPB + wave * kQPW + li;
@@ -420,25 +459,15 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     }
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    qamax = __builtin_fmaxf(qamax, __shfl_xor(qamax, o));
-    svmax = __builtin_fmaxf(svmax, __shfl_xor(svmax, o));
-  }
-  if (lane == 0) {
-    red[wave] = qamax;
-    red[kWaves + wave] = svmax;
-  }
+  for (int o = 32; o >= 1; o >>= 1) qamax = __builtin_fmaxf(qamax, __shfl_xor(qamax, o));
+  if (lane == 0) red[wave] = qamax;
   __syncthreads();
   qamax = 0.0f;
-  svmax = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    qamax = __builtin_fmaxf(qamax, red[w]);
-    svmax = __builtin_fmaxf(svmax, red[kWaves + w]);
-  }
+  for (int w = 0; w < kWaves; ++w) qamax = __builtin_fmaxf(qamax, red[w]);
   const float q_inv = qamax > 0.0f ? kFp8Max / qamax : 0.0f;
-  const float kscale = (qamax / kFp8Max) * (kLog2e / sqrtf((float)D));
-  const float inv_svmax = svmax > 0.0f ? 1.0f / svmax : 0.0f;
+  const float kscale = __builtin_fmaxf((qamax / kFp8Max) * (kLog2e / sqrtf((float)D)), kScaleMin);
+  const float inv_kscale = 1.0f / kscale;
 
   // ---- Q prologue pass 2: e4m3 codes in the B-operand layout ---------------
   // operand step s, byte b <-> d: D=128: d = 64 s + 32 hh + b; D=64: byte b < 16
@@ -595,10 +624,10 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   if (n_it > 0) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      load_tile<D>(regs, tref(clamp_it(p)), kc, vc, ks, vs, tid);
-      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale, inv_svmax, tid);
+      load_tile<D>(regs, tref(clamp_it(p)), kc, vc, frec, fu, tid);
+      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale, inv_kscale, tid);
     }
-    load_tile<D>(regs, tref(clamp_it(2)), kc, vc, ks, vs, tid);
+    load_tile<D>(regs, tref(clamp_it(2)), kc, vc, frec, fu, tid);
   }
   for (int i = tid; i < SM::V_BYTES / 16; i += kThreads)
     ((uint4*)(stage_of(-1) + SM::K_BYTES))[i] = make_uint4(0, 0, 0, 0);
@@ -627,8 +656,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     // next one) and the loads of tile it + 3; at the top of the iteration so
     // that its latency overlaps the products.  Unconditional with the tile
     // index clamped: past the end the copy lands in a stage nobody reads again
-    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(it + 2), kscale, inv_svmax, tid);
-    load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, ks, vs, tid);
+    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(it + 2), kscale, inv_kscale, tid);
+    load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, frec, fu, tid);
 
     // (1) the PV and row-sum products of tile it - 1, interleaved with the
     // scores of tile it: t = fma(S, kf, -m), a quarter (8 keys) per product
@@ -770,8 +799,28 @@ int attend_queries_per_block() { return kQPB; }
 // parts are bounded so that the workspace has a fixed size
 constexpr int kMaxParts = 512;
 int attend_max_parts() { return kMaxParts; }
-size_t attend_workspace_bytes(int head_dim) {
-  return (size_t)kMaxParts * kQPB * ((size_t)head_dim + 2) * sizeof(float);
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+static size_t partials_bytes(int head_dim) {
+  return align256((size_t)kMaxParts * kQPB * ((size_t)head_dim + 2) * sizeof(float));
+}
+size_t attend_workspace_bytes(int head_dim, int n_kv_heads, int64_t slots_padded) {
+  const size_t tiles = (size_t)n_kv_heads * (size_t)(slots_padded / 64);
+  return partials_bytes(head_dim) + align256((size_t)n_kv_heads * 4) + align256(tiles * 64 * 16) +
+         align256(tiles * 128);
+}
+void attend_set_workspace(AttendArgs& a, void* ws, int head_dim, int n_kv_heads, int64_t slots_padded) {
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  const size_t tiles = (size_t)n_kv_heads * (size_t)(slots_padded / 64);
+  a.ws_o = reinterpret_cast<float*>(p);
+  a.ws_ml = a.ws_o + (size_t)kMaxParts * kQPB * head_dim;
+  p += partials_bytes(head_dim);
+  a.fac_sv = reinterpret_cast<float*>(p);
+  p += align256((size_t)n_kv_heads * 4);
+  a.fac_l = reinterpret_cast<float*>(p);
+  p += align256(tiles * 64 * 16);
+  a.fac_u = p;
+  a.n_kv_heads = n_kv_heads;
+  a.ring_tiles = (int32_t)(slots_padded / 64);
 }
 
 hipError_t attend_capacity(int* workgroups) {
@@ -815,6 +864,7 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
   args.n_parts = rem * S;
   args.full_per_xcd = (args.n_full + 7) / 8;
   args.parts_per_xcd = (args.n_parts + 7) / 8;
+  hipLaunchKernelGGL(factors_kernel, dim3(args.n_kv_heads * kFactorParts), dim3(256), 0, stream, args);
   const dim3 g(8 * (args.full_per_xcd + args.parts_per_xcd)), b(kThreads);
 #define RTV_LAUNCH(DIM, MASK, QL, PL) \
   hipLaunchKernelGGL((attend_kernel<DIM, MASK, QL, PL>), g, b, 0, stream, args)

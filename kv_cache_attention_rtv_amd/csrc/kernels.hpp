@@ -51,13 +51,22 @@ struct AttendArgs {
   int32_t full_per_xcd;
   int32_t parts_per_xcd;
   int32_t n_parts;
-  float* ws_o;            // [n_parts][queries per workgroup][D] f32, O / c
-  float* ws_ml;           // [n_parts][queries per workgroup][2] f32 (m, l)
+  float* ws_o;            // [n_parts][queries per workgroup][D] f32, sum p V
+  float* ws_ml;           // [n_parts][queries per workgroup][2] f32 (m, sum p)
+  // per-window key factors (written by the factors kernel of the same call):
+  float* fac_sv;          // [n_kv_heads] max V scale over the window
+  float* fac_l;           // [n_kv_heads][ring tiles][64] float4 records (sk', log2(55 rho) / sk', 0, 0)
+  uint8_t* fac_u;         // [n_kv_heads][ring tiles][2][64] e4m3 rows of 2^-2 / rho
+  int32_t n_kv_heads;
+  int32_t ring_tiles;     // slots_padded / 64
 };
 
 // concurrent workgroups per device and workspace bound of the attention kernel
 int attend_max_parts();
-size_t attend_workspace_bytes(int head_dim);
+// workspace of rtv_attend: split-key-range partials and the per-window key
+// factors; attend_set_workspace points the arguments into it
+size_t attend_workspace_bytes(int head_dim, int n_kv_heads, int64_t slots_padded);
+void attend_set_workspace(AttendArgs& a, void* ws, int head_dim, int n_kv_heads, int64_t slots_padded);
 hipError_t attend_capacity(int* workgroups);
 
 hipError_t launch_append(const AppendArgs& args, int head_dim, hipStream_t stream);

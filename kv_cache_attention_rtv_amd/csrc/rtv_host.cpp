@@ -78,7 +78,7 @@ rtv_status make_plan(const rtv_config* c, Plan* p) {
   if (!mul_ok(rope_elems, 4, &tmp)) return RTV_ERR_INVALID_ARG;
   p->rope_bytes = align_up((size_t)tmp);
   // attention workspace (partial results of split key ranges), shared by all layers
-  p->ws_bytes = align_up(rtv::attend_workspace_bytes(c->head_dim));
+  p->ws_bytes = align_up(rtv::attend_workspace_bytes(c->head_dim, c->n_kv_heads, Sp));
   if (!mul_ok((int64_t)c->n_kv_heads * c->head_dim, Sp, &tmp)) return RTV_ERR_INVALID_ARG;
   p->codes_bytes = align_up((size_t)tmp);
   p->scales_bytes = align_up((size_t)c->n_kv_heads * (size_t)Sp * 4);
@@ -350,8 +350,7 @@ rtv_status rtv_attend(rtv_cache* c, int32_t layer, const void* q_bf16, int64_t q
   a.n_work = a.n_qtiles * cfg.n_q_heads;
   a.capacity = c->capacity;
   a.two_term_q = cfg.query_terms == 2;
-  a.ws_o = c->ws;
-  a.ws_ml = c->ws + (size_t)rtv::attend_max_parts() * qpb * cfg.head_dim;
+  rtv::attend_set_workspace(a, c->ws, cfg.head_dim, cfg.n_kv_heads, c->plan.slots_padded);
   if (rtv::launch_attend(a, cfg.head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
     return RTV_ERR_HIP;
   return RTV_OK;
