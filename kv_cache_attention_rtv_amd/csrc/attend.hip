@@ -25,16 +25,18 @@
 // Scores: the queries of a workgroup share one e4m3 scale s_q, so the whole
 // per-score scale folds into a per-key factor kf = sk * s_q * log2(e)/sqrt(D).
 // P' carries the V scale of its key: P' = p * 55 * rho_key with
-// rho = sv / (max sv over the window), so that P' . Vcodes * max sv / 55 is
-// the weighted sum of V.  log2(55 rho) enters as the accumulator's initial
-// value C = log2(55 rho) / kf, so t = fma(S, kf, -m) = log2 P' and P' is
-// one exp2 and one conversion per score.  The row sum is taken from the
-// same e4m3 P' by the matrix cores, against U = 1/rho as two e4m3 terms
-// (rows 0 and 1 of U): numerator and denominator share the rounding of P',
-// and a key's weight no longer depends on the size of its V row.  The
+// rho = sv / 2^e, 2^e the least power of two above the largest V scale of
+// the key's 64-slot tile; the PV product scales P' back by 2^e through the
+// E8M0 scale of its B operand (exact), so that it sums 55 p sv Vcodes.
+// log2(55 rho) enters as the accumulator's initial value
+// C = log2(55 rho) / kf, so t = fma(S, kf, -m) = log2 P' and P' is one exp2
+// and one conversion per score.  The row sum is taken from the same e4m3 P'
+// by the matrix cores, against U = 1/rho as two e4m3 terms (rows 0 and 1 of
+// U): numerator and denominator share the rounding of P'.  The per-key
+// factors come from a small factors kernel run before the attention.  The
 // running max m is lazy: it moves only when some P' would exceed 440, and
-// then leaves a factor 2^kTau of headroom.  Output O = acc * max sv / L,
-// rounded to bf16.
+// then leaves a factor 2^kTau of headroom.  Output O = acc / L, rounded to
+// bf16.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -116,8 +118,8 @@ struct Smem {
   // V^T rows, then the two U rows and a zero row (zeroed once, never staged)
   static constexpr int V_BYTES = (D + 3) * VROW;
   static constexpr int U_OFF = K_BYTES + D * VROW;
-  static constexpr int KF_OFF = K_BYTES + V_BYTES;    // kf[64], then C[64]
-  static constexpr int STAGE = KF_OFF + 2 * 64 * 4;
+  static constexpr int KF_OFF = K_BYTES + V_BYTES;    // kf[64], C[64], the tile's V exponent
+  static constexpr int STAGE = KF_OFF + 2 * 64 * 4 + 16;
 };
 
 // Staged tile: with 512 threads, threads 0..255 (waves 0-3) move the K rows
@@ -127,8 +129,9 @@ struct Smem {
 constexpr int kStageJobs = kThreads >= 512 ? 1 : 2;
 struct TileRegs {
   uint4 c[kStageJobs][2];
-  // K side: the factor record (max(sk, kScaleMin), log2(55 rho) / that, 0, 0)
-  // of key (thread & 63); V side: 16-byte piece (thread & 7) of the U rows
+  // K side: the factor record (max(sk, kScaleMin), log2(55 rho) / that, the
+  // tile's E8M0 V exponent, 0) of key (thread & 63); V side: 16-byte piece
+  // (thread & 7) of the U rows
   uint4 x[kStageJobs];
 };
 
@@ -234,62 +237,11 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, 
     float* kfp = (float*)(st + SM::KF_OFF);
     kfp[key] = ok ? kf : kMaskFactor;
     kfp[64 + key] = ok ? c : 0.0f;
+    if (key == 0) ((uint32_t*)kfp)[128] = xk.z;
   }
   if (vside) {
     const int piece = gt & 7;
     *(uint4*)(st + SM::U_OFF + (piece >> 2) * SM::VROW + 16 * (piece & 3)) = xv;
-  }
-}
-
-// Per-window key factors, one workgroup per (KV head, part of the window's
-// tiles); every workgroup first takes the window's max V scale svmax.  For
-// each slot of a window tile: rho = sv / svmax (1 for a zero V row, at least
-// kRhoMin), the record (sk' = max(sk, kScaleMin), log2(55 rho) / sk', 0, 0),
-// and the two e4m3 terms of 2^-2 / rho at the slot's byte position in the U
-// rows.  Slots of a partial
-// tile outside the window get factors too (from whatever their scales hold);
-// the attention masks them.
-constexpr int kFactorParts = 8;
-__global__ __launch_bounds__(256) void factors_kernel(AttendArgs a) {
-  __shared__ float red[4];
-  const int h = blockIdx.x / kFactorParts;
-  const int part = blockIdx.x % kFactorParts;
-  const int tid = threadIdx.x;
-  const int64_t Sp = a.slots_padded;
-  const float* ks = a.ks + (int64_t)h * Sp;
-  const float* vs = a.vs + (int64_t)h * Sp;
-  float svmax = 0.0f;
-  for (int s = 0; s < a.n_segments; ++s)
-    for (int64_t slot = a.seg_lo[s] + tid; slot < a.seg_hi[s]; slot += 256)
-      svmax = __builtin_fmaxf(svmax, vs[slot]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) svmax = __builtin_fmaxf(svmax, __shfl_xor(svmax, o));
-  if ((tid & 63) == 0) red[tid >> 6] = svmax;
-  __syncthreads();
-  svmax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
-  if (part == 0 && tid == 0) a.fac_sv[h] = svmax;
-  const float inv = svmax > 0.0f ? 1.0f / svmax : 0.0f;
-
-  float4* rec = (float4*)a.fac_l + (int64_t)h * a.ring_tiles * 64;
-  uint8_t* fu = a.fac_u + (int64_t)h * a.ring_tiles * 128;
-  const int key = tid & 63;
-  for (int s = 0; s < a.n_segments; ++s) {
-    if (a.seg_hi[s] <= a.seg_lo[s]) continue;
-    const int t0 = (int)(a.seg_lo[s] / 64), t1 = (int)((a.seg_hi[s] - 1) / 64);
-    for (int tile = t0 + part * 4 + (tid >> 6); tile <= t1; tile += kFactorParts * 4) {
-      const int64_t slot = (int64_t)tile * 64 + key;
-      const float sv = vs[slot];
-      const float sk = ks[slot];
-      const float rho = sv > 0.0f ? __builtin_fmaxf(sv * inv, kRhoMin) : 1.0f;
-      const float skf = __builtin_fmaxf(sk, kScaleMin);
-      rec[slot] = make_float4(skf, (kLogPW + __builtin_amdgcn_logf(rho)) / skf, 0.0f, 0.0f);
-      const float u = 0.25f / rho;
-      const int hi = __builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false);
-      const float uh = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false)[0];
-      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(u - uh, 0.0f, 0, false);
-      fu[(int64_t)tile * 128 + vt_pos(key)] = (uint8_t)hi;
-      fu[(int64_t)tile * 128 + 64 + vt_pos(key)] = (uint8_t)lo;
-    }
   }
 }
 
@@ -301,6 +253,53 @@ __device__ __forceinline__ TileRef tile_of(int it, int t_count0, int t_first0, i
   r.hi = second ? hi1 : hi0;
   r.tile = second ? t_first1 + (it - t_count0) : t_first0 + it;
   return r;
+}
+
+// Per-window key factors: one wave per (KV head, window tile).  The tile's V
+// exponent e is the least power of two 2^e >= its largest V scale; for each
+// slot rho = sv / 2^e (exact; 1 for a zero V row, at least kRhoMin), the
+// record (sk' = max(sk, kScaleMin), log2(55 rho) / sk', 127 + e, 0) and the
+// two e4m3 terms of 2^-2 / rho at the slot's byte position in the U rows.
+// Slots of a partial tile outside the window get factors too (from whatever
+// their scales hold; the attention masks them).
+__global__ __launch_bounds__(256) void factors_kernel(AttendArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lo0 = (int)a.seg_lo[0], hi0 = (int)a.seg_hi[0];
+  const int lo1 = a.n_segments > 1 ? (int)a.seg_lo[1] : 0;
+  const int hi1 = a.n_segments > 1 ? (int)a.seg_hi[1] : 0;
+  const int t_first0 = lo0 / 64;
+  const int t_count0 = hi0 > lo0 ? (hi0 - 1) / 64 - t_first0 + 1 : 0;
+  const int t_first1 = lo1 / 64;
+  const int t_count1 = hi1 > lo1 ? (hi1 - 1) / 64 - t_first1 + 1 : 0;
+  const int n_all = t_count0 + t_count1;
+  if (w >= n_all * a.n_kv_heads) return;      // whole waves leave together
+  const int h = w / n_all;
+  const int i = w % n_all;
+  const int tile = i < t_count0 ? t_first0 + i : t_first1 + (i - t_count0);
+  const int64_t slot = (int64_t)h * a.slots_padded + (int64_t)tile * 64 + lane;
+  const float sv = a.vs[slot];
+  const float sk = a.ks[slot];
+  // (non-finite or negative scales, which only unused slots could hold, count as 0)
+  float m = sv > 0.0f && sv <= 3.40282347e38f ? sv : 0.0f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+  int e = 0;
+  if (m > 0.0f) {
+    (void)frexpf(m, &e);                // m = f * 2^e, f in [0.5, 1): 2^e > m
+    e = e < -126 ? -126 : e;
+  }
+  const float rho = sv > 0.0f ? __builtin_fmaxf(ldexpf(sv, -e), kRhoMin) : 1.0f;
+  const float skf = __builtin_fmaxf(sk, kScaleMin);
+  const int64_t rt = (int64_t)h * a.ring_tiles + tile;
+  ((float4*)a.fac_l)[rt * 64 + lane] =
+      make_float4(skf, (kLogPW + __builtin_amdgcn_logf(rho)) / skf, __uint_as_float((uint32_t)(127 + e)), 0.0f);
+  const float u = 0.25f / rho;
+  const int hi = __builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false);
+  const float uh = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false)[0];
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(u - uh, 0.0f, 0, false);
+  a.fac_u[rt * 128 + vt_pos(lane)] = (uint8_t)hi;
+  a.fac_u[rt * 128 + 64 + vt_pos(lane)] = (uint8_t)lo;
 }
 
 // t = S_raw * kf - m for the 32 keys of this lane
@@ -434,7 +433,6 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   const uint8_t* vc = a.vc + (int64_t)kvh * Sp * D;
   const uint4* frec = (const uint4*)a.fac_l + (int64_t)kvh * a.ring_tiles * 64;
   const uint4* fu = (const uint4*)(a.fac_u + (int64_t)kvh * a.ring_tiles * 128);
-  const float svmax = a.fac_sv[kvh];   // window max of the V scales
 
   // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
   const int q_row = qtile * kQPB + wave * kQPW + li;
@@ -606,10 +604,12 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     }
   };
   // product j of the NDT + 1: d sub-tile j, or the row sum (j = NDT)
-  auto pv_step = [&](int j, const v8i (&vop)[NDT + 1], const v8i& pop, const v8i& plo) {
+  // (P' of a tile carries rho relative to the tile's 2^e: the V products
+  // scale it back by the E8M0 exponent ev = 127 + e)
+  auto pv_step = [&](int j, const v8i (&vop)[NDT + 1], const v8i& pop, const v8i& plo, int ev) {
     if (j < NDT) {
-      acc_o[j] = mfma_fp8(vop[j], pop, acc_o[j]);
-      if constexpr (PLO) acc_o[j] = mfma_fp8_bscaled(vop[j], plo, acc_o[j], 127 - kLoShift);
+      acc_o[j] = mfma_fp8_scaled(vop[j], pop, acc_o[j], 127, ev);
+      if constexpr (PLO) acc_o[j] = mfma_fp8_scaled(vop[j], plo, acc_o[j], 127, ev - kLoShift);
     } else {
       acc_l = mfma_fp8_scaled(vop[NDT], pop, acc_l, 127 + 2, 127);
       if constexpr (PLO) acc_l = mfma_fp8_scaled(vop[NDT], plo, acc_l, 127 + 2, 127 - kLoShift);
@@ -631,6 +631,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   }
   for (int i = tid; i < SM::V_BYTES / 16; i += kThreads)
     ((uint4*)(stage_of(-1) + SM::K_BYTES))[i] = make_uint4(0, 0, 0, 0);
+  if (tid == 0) ((int*)(stage_of(-1) + SM::KF_OFF))[128] = 127;
   if (tid < (kStages - 1) * (SM::VROW / 16))
     ((uint4*)(smem + (tid / (SM::VROW / 16)) * SM::STAGE + SM::U_OFF + 2 * SM::VROW))[tid % (SM::VROW / 16)] =
         make_uint4(0, 0, 0, 0);
@@ -667,10 +668,11 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     for (int w = 0; w < 8; ++w) kf4[w] = *(const float4*)(kf + 32 * (w >> 2) + 8 * (w & 3) + 4 * hh);
     v8i vop[NDT + 1];
     load_v(stage_of(it - 1), vop);
+    const int ev = __builtin_amdgcn_readfirstlane(((const int*)(stage_of(it - 1) + SM::KF_OFF))[128]);
     float t[32];
 #pragma unroll
     for (int c = 0; c < 4 || c <= NDT; ++c) {
-      if (c <= NDT) pv_step(c, vop, pop, plo);
+      if (c <= NDT) pv_step(c, vop, pop, plo, ev);
       if (c < 4) {
 #pragma unroll
         for (int w = 2 * c; w < 2 * c + 2; ++w) {
@@ -707,8 +709,9 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   {
     v8i vop[NDT + 1];
     load_v(stage_of(n_it - 1), vop);
+    const int ev = __builtin_amdgcn_readfirstlane(((const int*)(stage_of(n_it - 1) + SM::KF_OFF))[128]);
 #pragma unroll
-    for (int j = 0; j <= NDT; ++j) pv_step(j, vop, pop, plo);
+    for (int j = 0; j <= NDT; ++j) pv_step(j, vop, pop, plo, ev);
   }
 
   // ---- epilogue ----------------------------------------------------------------
@@ -720,7 +723,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     // with m
     const int q = wave * kQPW + li;
     float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
-    const float inv_c = svmax / kPW;
+    const float inv_c = 1.0f / kPW;
 #pragma unroll
     for (int d = 0; d < NDT; ++d)
 #pragma unroll
@@ -732,7 +735,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     if (hh == 0) *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) = make_float2(m_run, l_tot / kPW);
     return;
   }
-  const float scale = svmax / l_tot;
+  const float scale = 1.0f / l_tot;
   if (q_row < a.n_tokens) {
     uint16_t* dst = a.out + (int64_t)q_row * a.ldo + (int64_t)head * D;
 #pragma unroll
@@ -805,7 +808,7 @@ static size_t partials_bytes(int head_dim) {
 }
 size_t attend_workspace_bytes(int head_dim, int n_kv_heads, int64_t slots_padded) {
   const size_t tiles = (size_t)n_kv_heads * (size_t)(slots_padded / 64);
-  return partials_bytes(head_dim) + align256((size_t)n_kv_heads * 4) + align256(tiles * 64 * 16) +
+  return partials_bytes(head_dim) + align256(tiles * 64 * 16) +
          align256(tiles * 128);
 }
 void attend_set_workspace(AttendArgs& a, void* ws, int head_dim, int n_kv_heads, int64_t slots_padded) {
@@ -814,8 +817,6 @@ void attend_set_workspace(AttendArgs& a, void* ws, int head_dim, int n_kv_heads,
   a.ws_o = reinterpret_cast<float*>(p);
   a.ws_ml = a.ws_o + (size_t)kMaxParts * kQPB * head_dim;
   p += partials_bytes(head_dim);
-  a.fac_sv = reinterpret_cast<float*>(p);
-  p += align256((size_t)n_kv_heads * 4);
   a.fac_l = reinterpret_cast<float*>(p);
   p += align256(tiles * 64 * 16);
   a.fac_u = p;
@@ -864,7 +865,10 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
   args.n_parts = rem * S;
   args.full_per_xcd = (args.n_full + 7) / 8;
   args.parts_per_xcd = (args.n_parts + 7) / 8;
-  hipLaunchKernelGGL(factors_kernel, dim3(args.n_kv_heads * kFactorParts), dim3(256), 0, stream, args);
+  {
+    const int waves = n_tiles * args.n_kv_heads;
+    if (waves > 0) hipLaunchKernelGGL(factors_kernel, dim3((waves + 3) / 4), dim3(256), 0, stream, args);
+  }
   const dim3 g(8 * (args.full_per_xcd + args.parts_per_xcd)), b(kThreads);
 #define RTV_LAUNCH(DIM, MASK, QL, PL) \
   hipLaunchKernelGGL((attend_kernel<DIM, MASK, QL, PL>), g, b, 0, stream, args)

@@ -54,8 +54,7 @@ struct AttendArgs {
   float* ws_o;            // [n_parts][queries per workgroup][D] f32, sum p V
   float* ws_ml;           // [n_parts][queries per workgroup][2] f32 (m, sum p)
   // per-window key factors (written by the factors kernel of the same call):
-  float* fac_sv;          // [n_kv_heads] max V scale over the window
-  float* fac_l;           // [n_kv_heads][ring tiles][64] float4 records (sk', log2(55 rho) / sk', 0, 0)
+  float* fac_l;           // [n_kv_heads][ring tiles][64] float4 records (sk', log2(55 rho) / sk', 127 + e, 0)
   uint8_t* fac_u;         // [n_kv_heads][ring tiles][2][64] e4m3 rows of 2^-2 / rho
   int32_t n_kv_heads;
   int32_t ring_tiles;     // slots_padded / 64
