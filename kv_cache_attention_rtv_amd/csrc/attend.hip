@@ -140,19 +140,30 @@ struct TileRef {
   int lo, hi;         // the segment the tile belongs to (slot indices fit in int32)
 };
 
+// dword 3 of a raw buffer descriptor (32-bit elements, no swizzle)
+constexpr int kBufferFlags = 0x00020000;
+
+// The side (K or V) of a thread is uniform over its wave (side = -1 for
+// 256-thread workgroups, where every thread does both); the addresses are a
+// wave-uniform base plus a per-lane offset that does not change with the tile.
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const uint8_t* kc,
-                                          const uint8_t* vc, const uint4* frec, const uint4* fu,
-                                          int tid) {
+                                          const uint8_t* vc, const uint8_t* frec, const uint8_t* fu,
+                                          int side, int code_off, int xk_off, int xv_off) {
   constexpr int LD_BYTES = D / 4;
-  const int gt = tid & 255;
 #pragma unroll
   for (int j = 0; j < kStageJobs; ++j) {
-    const bool isv = kStageJobs == 1 ? tid >= 256 : j == 1;
-    const uint8_t* src = (isv ? vc : kc) + (int64_t)t.tile * 64 * D + gt * LD_BYTES;
-    r.c[j][0] = *(const uint4*)(src);
-    if constexpr (LD_BYTES == 32) r.c[j][1] = *(const uint4*)(src + 16);
-    r.x[j] = isv ? fu[(int64_t)t.tile * 8 + (gt & 7)] : frec[(int64_t)t.tile * 64 + (gt & 63)];
+    const bool isv = kStageJobs == 1 ? side == 1 : j == 1;
+    // buffer loads through a descriptor of exactly this tile's bytes
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((isv ? vc : kc) + (int64_t)t.tile * 64 * D), 0, 64 * D, kBufferFlags);
+    r.c[j][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, code_off, 0, 0));
+    if constexpr (LD_BYTES == 32)
+      r.c[j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, code_off + 16, 0, 0));
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(isv ? fu + (int64_t)t.tile * 128 : frec + (int64_t)t.tile * 1024), 0, isv ? 128 : 1024,
+        kBufferFlags);
+    r.x[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, isv ? xv_off : xk_off, 0, 0));
   }
 }
 
@@ -431,8 +442,11 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   const int64_t Sp = a.slots_padded;
   const uint8_t* kc = a.kc + (int64_t)kvh * Sp * D;
   const uint8_t* vc = a.vc + (int64_t)kvh * Sp * D;
-  const uint4* frec = (const uint4*)a.fac_l + (int64_t)kvh * a.ring_tiles * 64;
-  const uint4* fu = (const uint4*)(a.fac_u + (int64_t)kvh * a.ring_tiles * 128);
+  const uint8_t* frec = (const uint8_t*)a.fac_l + (int64_t)kvh * a.ring_tiles * 1024;
+  const uint8_t* fu = a.fac_u + (int64_t)kvh * a.ring_tiles * 128;
+  const int side = kStageJobs == 1 ? (__builtin_amdgcn_readfirstlane(tid) >= 256 ? 1 : 0) : -1;
+  const int code_off = (tid & 255) * (D / 4);
+  const int xk_off = (tid & 63) * 16, xv_off = (tid & 7) * 16;
 
   // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
   const int q_row = qtile * kQPB + wave * kQPW + li;
@@ -624,10 +638,10 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   if (n_it > 0) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      load_tile<D>(regs, tref(clamp_it(p)), kc, vc, frec, fu, tid);
+      load_tile<D>(regs, tref(clamp_it(p)), kc, vc, frec, fu, side, code_off, xk_off, xv_off);
       store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale, inv_kscale, tid);
     }
-    load_tile<D>(regs, tref(clamp_it(2)), kc, vc, frec, fu, tid);
+    load_tile<D>(regs, tref(clamp_it(2)), kc, vc, frec, fu, side, code_off, xk_off, xv_off);
   }
   for (int i = tid; i < SM::V_BYTES / 16; i += kThreads)
     ((uint4*)(stage_of(-1) + SM::K_BYTES))[i] = make_uint4(0, 0, 0, 0);
@@ -651,28 +665,30 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   // ---- main loop: iteration it computes the softmax of tile it while the
   // matrix cores take the PV product of tile it - 1 and the scores of tile
   // it + 1; the ring holds tiles it - 1 .. it + 2
-  for (int it = 0; it < n_it; ++it) {
+  // one iteration; r = it mod 4 (a constant after the unrolling below), so
+  // that every LDS address is a lane base plus an immediate offset
+  auto tile_step = [&](const int it, const int r) __attribute__((always_inline)) {
     // (0) staging of tile it + 2 into the stage that tile it - 2 held (last
     // read before the previous barrier; first read of tile it + 2 after the
     // next one) and the loads of tile it + 3; at the top of the iteration so
     // that its latency overlaps the products.  Unconditional with the tile
     // index clamped: past the end the copy lands in a stage nobody reads again
-    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(it + 2), kscale, inv_kscale, tid);
-    load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, frec, fu, tid);
+    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(r + 2), kscale, inv_kscale, tid);
+    load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, frec, fu, side, code_off, xk_off, xv_off);
 
     // (1) the PV and row-sum products of tile it - 1, interleaved with the
     // scores of tile it: t = fma(S, kf, -m), a quarter (8 keys) per product
-    const float* kf = (const float*)(stage_of(it) + SM::KF_OFF);
+    const float* kf = (const float*)(stage_of(r) + SM::KF_OFF);
     float4 kf4[8];
 #pragma unroll
     for (int w = 0; w < 8; ++w) kf4[w] = *(const float4*)(kf + 32 * (w >> 2) + 8 * (w & 3) + 4 * hh);
     v8i vop[NDT + 1];
-    load_v(stage_of(it - 1), vop);
-    const int ev = __builtin_amdgcn_readfirstlane(((const int*)(stage_of(it - 1) + SM::KF_OFF))[128]);
+    load_v(stage_of(r + 3), vop);
+    const int ev = __builtin_amdgcn_readfirstlane(((const int*)(stage_of(r + 3) + SM::KF_OFF))[128]);
     float t[32];
 #pragma unroll
     for (int c = 0; c < 4 || c <= NDT; ++c) {
-      if (c <= NDT) pv_step(c, vop, pop, plo, ev);
+      // vector work first: the operand reads of the product land meanwhile
       if (c < 4) {
 #pragma unroll
         for (int w = 2 * c; w < 2 * c + 2; ++w) {
@@ -681,20 +697,22 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
           for (int e = 0; e < 4; ++e) t[4 * w + e] = __builtin_fmaf(acc_s[w >> 2][4 * (w & 3) + e], kk[e], -m_run);
         }
       }
+      if (c <= NDT) pv_step(c, vop, pop, plo, ev);
       chunk_fence();
     }
-    const float mx = xhalf_max(max32(t));
+    // (any lane over the bound triggers: no cross-half max needed here)
+    const float mx = max32(t);
     lazy_rescale<NDT>(acc_s, kf, hh, mx, m_run, acc_o, acc_l, t);
 
     // (2) the score products of tile it + 1 (past the last tile they read a
     // stale stage and are unused), interleaved with P' of tile it
     {
       v8i kop[2][NSTEP];
-      load_k(stage_of(it + 1), kop, acc_s);
+      load_k(stage_of(r + 1), kop, acc_s);
 #pragma unroll
       for (int c = 0; c < 4 || c < 2 * NSTEP; ++c) {
-        if (c < 2 * NSTEP) qk_step(c, kop, acc_s);
         if (c < 4) probs_quarter<PLO>(c, t, pop, plo);
+        if (c < 2 * NSTEP) qk_step(c, kop, acc_s);
         chunk_fence();
       }
     }
@@ -705,6 +723,11 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     if constexpr (MASK) mask_scores(it + 1, acc_s);
 
     __syncthreads();
+  };
+  for (int it0 = 0; it0 < n_it; it0 += kStages) {
+#pragma unroll
+    for (int r = 0; r < kStages; ++r)
+      if (it0 + r < n_it) tile_step(it0 + r, r);
   }
   {
     v8i vop[NDT + 1];
