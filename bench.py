@@ -57,6 +57,7 @@ def parse():
 KERNEL_SOURCES = {
     "attend_kernel": "kv_cache_attention_rtv_amd/csrc/attend.hip",
     "combine_kernel": "kv_cache_attention_rtv_amd/csrc/attend.hip",
+    "factors_kernel": "kv_cache_attention_rtv_amd/csrc/attend.hip",
     "append_rope_quant_kernel": "kv_cache_attention_rtv_amd/csrc/append.hip",
 }
 
@@ -297,12 +298,14 @@ def main():
     # steady-state window) and per append, from the calibrated counters
     att_traffic = traffic_of(args.traffic_json, "attend_kernel<128, false, false, false>")
     comb_traffic = traffic_of(args.traffic_json, "combine_kernel<128>")
+    fac_traffic = traffic_of(args.traffic_json, "factors_kernel")
     app_traffic = traffic_of(args.traffic_json, "append_rope_quant_kernel<128>")
     traffic = None
     if att_traffic:
         traffic = sum(v["bytes"] for v in att_traffic.values())
-        if comb_traffic:
-            traffic += sum(v["bytes"] for v in comb_traffic.values())
+        for extra in (comb_traffic, fac_traffic):
+            if extra:
+                traffic += sum(v["bytes"] for v in extra.values())
     app_bytes_measured = sum(v["bytes"] for v in app_traffic.values()) if app_traffic else None
 
     result = {
@@ -327,7 +330,8 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "rtv_attend = attend_kernel<128, false, false, false> + combine_kernel<128>",
+            "kernel": ("rtv_attend = factors_kernel + attend_kernel<128, false, false, false> + "
+                       "combine_kernel<128>"),
             "achieved": round(att_tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
             "avg_launch_ms": round(att_avg_ms, 4),

@@ -157,6 +157,10 @@ rtv_status rtv_append_rope_quant(rtv_cache* cache, int32_t layer,
  *   out_bf16: [n_tokens][n_q_heads][D] bf16, row stride out_tok_stride
  *   max_window_frames: 0 = all valid frames; otherwise caps W (>= chunk_frames)
  * The append of this step must be ordered before this call on `stream`.
+ * Every attention call on one cache (any layer) uses the same workspace in the
+ * cache's arena (per-window key factors and partial results of split key
+ * ranges): calls that could overlap on the GPU must be ordered, e.g. on one
+ * stream.
  * Errors: INVALID_ARG, STATE (no append since the last advance). */
 rtv_status rtv_attend(rtv_cache* cache, int32_t layer,
                       const void* q_bf16, int64_t q_tok_stride,
