@@ -7,8 +7,9 @@
 // time", fourth paragraph; page "Runway: Πώς ένα AI 57 δισ. παραμέτρων
 // παράγει βίντεο στα 24 fps", section "Από οκτώ H100 σε τέσσερις").
 //
-// One workgroup = one 64-slot tile of the ring x one KV head (256 threads).
-// Eight lanes share a token row: lane g of the row holds the element groups
+// One workgroup = one 64-slot tile of the ring x three KV heads (512 threads,
+// 8 lanes per slot).  The RoPE (cos, sin) of a slot is loaded once and
+// applied to the K rows of all three heads.  Eight lanes share a token row: lane g of the row holds the element groups
 // [g*E, g*E+E) and [D/2+g*E, D/2+g*E+E), E = D/16, i.e. both halves of its
 // RoPE pairs, so the rotation needs no lane exchange and every bf16 load is
 // 8 lanes x 16 B = 128 B contiguous.  The row amax is an 8-lane DPP max.
@@ -26,7 +27,8 @@
 namespace rtv {
 namespace {
 
-constexpr int kAppendThreads = 256;
+constexpr int kAppendThreads = 512;   // 8 lanes per slot of a 64-slot tile
+constexpr int kAppendHeads = 3;       // KV heads per workgroup (share the RoPE loads)
 
 __device__ __forceinline__ float dpp_max8(float x) {
   // max over the 8 lanes of each row group: quad xor 1, quad xor 2, then the
@@ -83,19 +85,19 @@ __device__ __forceinline__ RowPiece<D / 16> load_piece(const uint16_t* row, int 
   return r;
 }
 
-template <int D>
+template <int D, int HPW>
 __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(AppendArgs a) {
   constexpr int E = D / 16;          // elements per lane per half
   constexpr int HALF = D / 2;
   constexpr int LDS_STRIDE = D + 4;  // bytes per V row in LDS
-  constexpr int ROWS = kAppendThreads / 8;           // rows per pass
-  constexpr int PASSES = kTileKeys / ROWS;
-  __shared__ uint32_t vrow[kTileKeys * LDS_STRIDE / 4];
+  static_assert(kAppendThreads == 8 * kTileKeys, "one lane octet per slot of the tile");
+  __shared__ uint32_t vrow[HPW][kTileKeys * LDS_STRIDE / 4];
 
+  const int groups = (a.n_heads + HPW - 1) / HPW;
   const int u = xcd_remap(blockIdx.x, a.n_work);
   if (u < 0) return;
-  const int st = a.first_tile + u / a.n_heads;
-  const int h = u % a.n_heads;
+  const int st = a.first_tile + u / groups;
+  const int h0 = (u % groups) * HPW;
   const int64_t tile_lo = (int64_t)st * kTileKeys;
   const int64_t lo = tile_lo > a.write_slot ? tile_lo : a.write_slot;
   const int64_t end = a.write_slot + a.n_tokens;
@@ -103,42 +105,45 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
 
   const int tid = threadIdx.x;
   const int g = tid & 7;
+  const int r = tid >> 3;                        // key row within the tile
+  const int64_t slot = tile_lo + r;
+  const bool valid = slot >= lo && slot < hi;
+  const int64_t t = valid ? slot - a.write_slot : 0;   // token in the chunk
 
-  // ---- issue every global load of both passes before any arithmetic -------
-  RowPiece<E> kp[PASSES], vp[PASSES];
-  float4 cs[PASSES][E / 2];
-  bool valid[PASSES];
-  int64_t slot[PASSES];
+  // ---- issue every global load before any arithmetic: the K and V pieces of
+  // the group's heads and, once for all of them, the row's RoPE (cos, sin) ----
+  RowPiece<E> kp[HPW], vp[HPW];
 #pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass) {
-    const int r = pass * ROWS + (tid >> 3);          // key row within the tile
-    slot[pass] = tile_lo + r;
-    valid[pass] = slot[pass] >= lo && slot[pass] < hi;
-    const int64_t t = valid[pass] ? slot[pass] - a.write_slot : 0;   // token in the chunk
-    kp[pass] = load_piece<D>(a.k + t * a.ldk + (int64_t)h * D, g, valid[pass]);
-    vp[pass] = load_piece<D>(a.v + t * a.ldv + (int64_t)h * D, g, valid[pass]);
+  for (int j = 0; j < HPW; ++j) {
+    const bool hv = h0 + j < a.n_heads;
+    kp[j] = load_piece<D>(a.k + t * a.ldk + (int64_t)(h0 + j) * D, g, valid && hv);
+    vp[j] = load_piece<D>(a.v + t * a.ldv + (int64_t)(h0 + j) * D, g, valid && hv);
+  }
+  float4 cs[E / 2];
+  {
     const float4* tab = (const float4*)(a.rope + (t * HALF + g * E) * 2);
 #pragma unroll
-    for (int i = 0; i < E / 2; ++i) cs[pass][i] = valid[pass] ? tab[i] : make_float4(1.f, 0.f, 1.f, 0.f);
+    for (int i = 0; i < E / 2; ++i) cs[i] = valid ? tab[i] : make_float4(1.f, 0.f, 1.f, 0.f);
   }
 
 #pragma unroll
-  for (int pass = 0; pass < PASSES; ++pass) {
-    const int r = pass * ROWS + (tid >> 3);
+  for (int j = 0; j < HPW; ++j) {
+    const int h = h0 + j;
+    if (h >= a.n_heads) break;                   // uniform over the workgroup
     // ---- K: rotate, quantize, store ------------------------------------
     {
       float r0[E], r1[E];
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < E / 2; ++i) {
-        const float4 c = cs[pass][i];                 // (cos, sin) of two pairs
+        const float4 c = cs[i];                  // (cos, sin) of two pairs
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int e = 2 * i + j;
-          const float co = j ? c.z : c.x;
-          const float si = j ? c.w : c.y;
-          const float x0 = (e & 1) ? bf16_hi(kp[pass].w0[e >> 1]) : bf16_lo(kp[pass].w0[e >> 1]);
-          const float x1 = (e & 1) ? bf16_hi(kp[pass].w1[e >> 1]) : bf16_lo(kp[pass].w1[e >> 1]);
+        for (int q = 0; q < 2; ++q) {
+          const int e = 2 * i + q;
+          const float co = q ? c.z : c.x;
+          const float si = q ? c.w : c.y;
+          const float x0 = (e & 1) ? bf16_hi(kp[j].w0[e >> 1]) : bf16_lo(kp[j].w0[e >> 1]);
+          const float x1 = (e & 1) ? bf16_hi(kp[j].w1[e >> 1]) : bf16_lo(kp[j].w1[e >> 1]);
           const float a0 = x0 * co;
           const float b0 = x1 * si;
           const float a1 = x1 * co;
@@ -150,8 +155,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
       }
       amax = dpp_max8(amax);
       const RowQuant q = row_quant(amax);
-      if (valid[pass]) {
-        uint8_t* dst = a.kc + ((int64_t)h * a.slots_padded + slot[pass]) * D;
+      if (valid) {
+        uint8_t* dst = a.kc + ((int64_t)h * a.slots_padded + slot) * D;
         if constexpr (E == 8) {
           uint2 c0, c1;
           c0.x = quant4(r0[0], r0[1], r0[2], r0[3], q);
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
           *(uint32_t*)(dst + g * E) = quant4(r0[0], r0[1], r0[2], r0[3], q);
           *(uint32_t*)(dst + HALF + g * E) = quant4(r1[0], r1[1], r1[2], r1[3], q);
         }
-        if (g == 0) a.ks[(int64_t)h * a.slots_padded + slot[pass]] = q.s;
+        if (g == 0) a.ks[(int64_t)h * a.slots_padded + slot] = q.s;
       }
     }
     // ---- V: quantize, stage row-major in LDS ----------------------------
@@ -172,63 +177,67 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
       float x0[E], x1[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        x0[e] = (e & 1) ? bf16_hi(vp[pass].w0[e >> 1]) : bf16_lo(vp[pass].w0[e >> 1]);
-        x1[e] = (e & 1) ? bf16_hi(vp[pass].w1[e >> 1]) : bf16_lo(vp[pass].w1[e >> 1]);
+        x0[e] = (e & 1) ? bf16_hi(vp[j].w0[e >> 1]) : bf16_lo(vp[j].w0[e >> 1]);
+        x1[e] = (e & 1) ? bf16_hi(vp[j].w1[e >> 1]) : bf16_lo(vp[j].w1[e >> 1]);
       }
       float amax = 0.0f;
 #pragma unroll
       for (int e = 0; e < E; ++e) amax = fmaxf(amax, fmaxf(fabsf(x0[e]), fabsf(x1[e])));
       amax = dpp_max8(amax);
       const RowQuant q = row_quant(amax);
-      uint32_t* row = vrow + r * (LDS_STRIDE / 4);
+      uint32_t* row = vrow[j] + r * (LDS_STRIDE / 4);
 #pragma unroll
       for (int i = 0; i < E / 4; ++i) {
         row[(g * E) / 4 + i] = quant4(x0[4 * i], x0[4 * i + 1], x0[4 * i + 2], x0[4 * i + 3], q);
         row[(HALF + g * E) / 4 + i] = quant4(x1[4 * i], x1[4 * i + 1], x1[4 * i + 2], x1[4 * i + 3], q);
       }
-      if (valid[pass] && g == 0) a.vs[(int64_t)h * a.slots_padded + slot[pass]] = q.s;
+      if (valid && g == 0) a.vs[(int64_t)h * a.slots_padded + slot] = q.s;
     }
   }
   __syncthreads();
 
-  // ---- V: transposed write of the tile ------------------------------------
+  // ---- V: transposed write of each head's tile ----------------------------
   // Thread block (p4, dq): positions 4*p4..4*p4+3 (4 consecutive keys) x
   // d = 4*dq..4*dq+3; a 4x4 byte transpose turns 4 key rows into 4 d rows.
-  uint8_t* vt = a.vc + (((int64_t)h * (a.slots_padded / kTileKeys) + st) * D) * kTileKeys;
   const bool full = (lo == tile_lo) && (hi == tile_lo + kTileKeys);
   constexpr int kBlocks = 16 * (D / 4);
 #pragma unroll
-  for (int it = 0; it < kBlocks / kAppendThreads; ++it) {
-    const int id = it * kAppendThreads + tid;
-    const int p4 = id & 15;
-    const int dq = id >> 4;
-    const int key0 = vt_key_of_pos4(p4);
-    const uint32_t a0 = vrow[(key0 + 0) * (LDS_STRIDE / 4) + dq];
-    const uint32_t a1 = vrow[(key0 + 1) * (LDS_STRIDE / 4) + dq];
-    const uint32_t a2 = vrow[(key0 + 2) * (LDS_STRIDE / 4) + dq];
-    const uint32_t a3 = vrow[(key0 + 3) * (LDS_STRIDE / 4) + dq];
-    const uint32_t lo01 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
-    const uint32_t hi01 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
-    const uint32_t lo23 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
-    const uint32_t hi23 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-    const uint32_t o[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
-                           __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
-                           __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
-                           __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
-    if (full) {
+  for (int j = 0; j < HPW; ++j) {
+    const int h = h0 + j;
+    if (h >= a.n_heads) break;
+    uint8_t* vt = a.vc + (((int64_t)h * (a.slots_padded / kTileKeys) + st) * D) * kTileKeys;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *(uint32_t*)(vt + (int64_t)(4 * dq + e) * kTileKeys + 4 * p4) = o[e];
-    } else {
-      // partial tile (chunk not aligned to 64 slots): write only this chunk's keys
+    for (int id = tid; id < kBlocks; id += kAppendThreads) {
+      const int p4 = id & 15;
+      const int dq = id >> 4;
+      const int key0 = vt_key_of_pos4(p4);
+      const uint32_t a0 = vrow[j][(key0 + 0) * (LDS_STRIDE / 4) + dq];
+      const uint32_t a1 = vrow[j][(key0 + 1) * (LDS_STRIDE / 4) + dq];
+      const uint32_t a2 = vrow[j][(key0 + 2) * (LDS_STRIDE / 4) + dq];
+      const uint32_t a3 = vrow[j][(key0 + 3) * (LDS_STRIDE / 4) + dq];
+      const uint32_t lo01 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+      const uint32_t o[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                             __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                             __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                             __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+      if (full) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+        for (int e = 0; e < 4; ++e)
+          *(uint32_t*)(vt + (int64_t)(4 * dq + e) * kTileKeys + 4 * p4) = o[e];
+      } else {
+        // partial tile (chunk not aligned to 64 slots): write only this chunk's keys
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int64_t slot = tile_lo + key0 + c;
-          if (slot >= lo && slot < hi)
-            vt[(int64_t)(4 * dq + e) * kTileKeys + 4 * p4 + c] = (uint8_t)(o[e] >> (8 * c));
-        }
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int64_t sl = tile_lo + key0 + c;
+            if (sl >= lo && sl < hi)
+              vt[(int64_t)(4 * dq + e) * kTileKeys + 4 * p4 + c] = (uint8_t)(o[e] >> (8 * c));
+          }
+      }
     }
   }
 }
@@ -252,12 +261,18 @@ __global__ void encode_e4m3_kernel(const float* __restrict__ x, uint8_t* __restr
 
 }  // namespace
 
-hipError_t launch_append(const AppendArgs& args, int head_dim, hipStream_t stream) {
+hipError_t launch_append(const AppendArgs& args_in, int head_dim, hipStream_t stream) {
+  // work items: (tile, group of kAppendHeads heads); args_in.n_work counts (tile, head)
+  AppendArgs args = args_in;
+  const int tiles = args.n_work / args.n_heads;
+  args.n_work = tiles * ((args.n_heads + kAppendHeads - 1) / kAppendHeads);
   const int blocks = ((args.n_work + 7) / 8) * 8;
   if (head_dim == 128)
-    hipLaunchKernelGGL(append_rope_quant_kernel<128>, dim3(blocks), dim3(kAppendThreads), 0, stream, args);
+    hipLaunchKernelGGL((append_rope_quant_kernel<128, kAppendHeads>), dim3(blocks), dim3(kAppendThreads), 0,
+                       stream, args);
   else
-    hipLaunchKernelGGL(append_rope_quant_kernel<64>, dim3(blocks), dim3(kAppendThreads), 0, stream, args);
+    hipLaunchKernelGGL((append_rope_quant_kernel<64, kAppendHeads>), dim3(blocks), dim3(kAppendThreads), 0,
+                       stream, args);
   return hipGetLastError();
 }
 
