@@ -54,8 +54,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 #endif
 constexpr int kWaves = RTV_ATTEND_WAVES;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kQPW = 32;                    // queries per wave
-constexpr int kQPB = kWaves * kQPW;         // queries per workgroup
+constexpr int kQPB = 256;                   // queries per workgroup
+constexpr int kQPW = kQPB / kWaves;         // queries per wave
+constexpr int kSub = kQPW / 32;             // 32-query sub-tiles per wave (they share the K/V operands)
 constexpr int kStages = 4;                  // LDS ring: tiles it - 1 .. it + 2
 constexpr float kTau = 3.0f;
 constexpr float kLogPmax = 8.78135971f;     // log2(440): bound on P' (below the e4m3 max 448)
@@ -342,26 +343,23 @@ __device__ __forceinline__ float max32(const float (&t)[32]) {
 }
 
 // Softmax of one 32-query tile over one 64-key tile, first half (after
-// t = fma(S, kf, -m), mx = the tile max of t): the lazy running-max update.
-// Rare: only when some P' would exceed 440 (always on the first tile, where
-// m = -inf makes every t = +inf); it rescales the O and row-sum
-// accumulators and leaves the largest P' of the tile at 440 / 2^kTau.
+// t = fma(S, kf, -m), mx = the lane's max of t): the lazy running-max update.
+// Rare: only when some P' would exceed 440; it rescales the O and row-sum
+// accumulators, shifts t and leaves the largest P' of the row at 440 / 2^kTau.
+// m is finite from the first tile on (set from tile 0 before the loop), so
+// the raw row max is max(t) + m and no score is recomputed.
 template <int NDT>
-__device__ __forceinline__ void lazy_rescale(const v16f (&s)[2], const float* kf, int hh, float mx,
-                                             float& m, v16f (&o)[NDT], v16f& lsum, float (&t)[32]) {
+__device__ __forceinline__ void lazy_rescale(float mx, float& m, v16f (&o)[NDT], v16f& lsum, float (&t)[32]) {
   if (__builtin_expect(__any(mx > kLogPmax), 0)) {
-    scores(s, kf, hh, 0.0f, t);   // raw log2 P' before the shift by m
-    float raw = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) raw = __builtin_fmaxf(raw, t[j]);
-    raw = xhalf_max(raw);
+    const float raw = xhalf_max(mx) + m;
     const float m_new = __builtin_fmaxf(m, raw - (kLogPmax - kTau));
-    const float alpha = exp2f(m - m_new);           // 0 on the first tile (m = -inf)
+    const float shift = m - m_new;
+    const float alpha = exp2f(shift);
 #pragma unroll
     for (int d = 0; d < NDT; ++d) o[d] *= alpha;
     lsum *= alpha;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) t[j] -= m_new;
+    for (int j = 0; j < 32; ++j) t[j] += shift;
     m = m_new;
   }
 }
@@ -449,25 +447,30 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   const int xk_off = (tid & 63) * 16, xv_off = (tid & 7) * 16;
 
   // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
-  const int q_row = qtile * kQPB + wave * kQPW + li;
-  const int src_row = q_row < a.n_tokens ? q_row : a.n_tokens - 1;
-  const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
-  const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
+  int q_rows[kSub];
   float qamax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < P; j += 8) {
-    const uint4 w0 = *(const uint4*)(q_src + P * hh + j);
-    const uint4 w1 = *(const uint4*)(q_src + D / 2 + P * hh + j);
-    const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
-    const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
+  for (int sub = 0; sub < kSub; ++sub) {
+    const int row = qtile * kQPB + wave * kQPW + sub * 32 + li;
+    q_rows[sub] = row;
+    const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
+    const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
+    const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
-      const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
-      const float2 c = *(const float2*)(q_cs + 2 * (j + e));
-      const float r0 = x0 * c.x - x1 * c.y;
-      const float r1 = x1 * c.x + x0 * c.y;
-      qamax = __builtin_fmaxf(qamax, __builtin_fmaxf(fabsf(r0), fabsf(r1)));
+    for (int j = 0; j < P; j += 8) {
+      const uint4 w0 = *(const uint4*)(q_src + P * hh + j);
+      const uint4 w1 = *(const uint4*)(q_src + D / 2 + P * hh + j);
+      const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
+      const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
+        const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
+        const float2 c = *(const float2*)(q_cs + 2 * (j + e));
+        const float r0 = x0 * c.x - x1 * c.y;
+        const float r1 = x1 * c.x + x0 * c.y;
+        qamax = __builtin_fmaxf(qamax, __builtin_fmaxf(fabsf(r0), fabsf(r1)));
+      }
     }
   }
 #pragma unroll
@@ -484,9 +487,14 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   // ---- Q prologue pass 2: e4m3 codes in the B-operand layout ---------------
   // operand step s, byte b <-> d: D=128: d = 64 s + 32 hh + b; D=64: byte b < 16
   // -> d = 16 hh + b, b >= 16 -> d = 32 + 16 hh + b - 16 (RoPE pairs stay in-lane)
-  v8i qop[NSTEP];
-  v8i qlo[NSTEP];
-  {
+  v8i qop[kSub][NSTEP];
+  v8i qlo[kSub][NSTEP];
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+    const int row = q_rows[sub];
+    const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
+    const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
+    const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
     float r0[P], r1[P];
 #pragma unroll
     for (int j = 0; j < P; j += 8) {
@@ -520,8 +528,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
         c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
         c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], (int)c, true);
       }
-      qop[w / 8][w % 8] = (int)c;
-      qlo[w / 8][w % 8] = (int)lo;
+      qop[sub][w / 8][w % 8] = (int)c;
+      qlo[sub][w / 8][w % 8] = (int)lo;
     }
   }
 
@@ -544,10 +552,10 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   auto clamp_it = [&](int it) { return it < n_it ? it : n_it - 1; };
   auto stage_of = [&](int it) { return smem + (it & (kStages - 1)) * SM::STAGE; };
 
-  // S^T = K . Q^T + C of the tile in stage st: K operands, the accumulator
-  // initial value C of the lane's 32 keys, and product j (key half j % 2,
-  // k-step j / 2) of the 2 * NSTEP
-  auto load_k = [&](const uint8_t* st, v8i (&kop)[2][NSTEP], v16f (&acc)[2]) {
+  // S^T = K . Q^T + C of the tile in stage st: the K operands (shared by the
+  // sub-tiles), the accumulator initial value C of the lane's 32 keys, and
+  // product j (key half j % 2, k-step j / 2) of the 2 * NSTEP of one sub-tile
+  auto load_kop = [&](const uint8_t* st, v8i (&kop)[2][NSTEP]) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       const uint8_t* krow = st + (32 * kh + li) * SM::KROW;
@@ -565,6 +573,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
                          (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
       }
     }
+  };
+  auto load_c = [&](const uint8_t* st, v16f (&acc)[2]) {
     const float* cp = (const float*)(st + SM::KF_OFF) + 64;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -577,10 +587,10 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
         acc[kh][4 * g + 3] = c4.w;
       }
   };
-  auto qk_step = [&](int j, const v8i (&kop)[2][NSTEP], v16f (&acc)[2]) {
+  auto qk_step = [&](int j, int sub, const v8i (&kop)[2][NSTEP], v16f (&acc)[2]) {
     const int kh = j & 1, s = j >> 1;
-    acc[kh] = mfma_fp8(kop[kh][s], qop[s], acc[kh]);
-    if constexpr (QLO) acc[kh] = mfma_fp8_bscaled(kop[kh][s], qlo[s], acc[kh], 127 - kLoShift);
+    acc[kh] = mfma_fp8(kop[kh][s], qop[sub][s], acc[kh]);
+    if constexpr (QLO) acc[kh] = mfma_fp8_bscaled(kop[kh][s], qlo[sub][s], acc[kh], 127 - kLoShift);
   };
   // keys of tile it outside its segment: add -448 * 448 to their raw scores
   // with one MFMA per key half (A: -448 at one k position of a masked key row,
@@ -601,11 +611,16 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   };
   // O^T += V^T . P'^T with the V tile in stage st, and the row sum
   // L += U . P'^T: lanes of rows 0 and 1 read the U rows of the stage, the
-  // others a zero row
-  v16f acc_o[NDT];
+  // others a zero row.  (P' of a tile carries rho relative to the tile's 2^e:
+  // the V products scale it back by the E8M0 exponent ev = 127 + e.)
+  v16f acc_o[kSub][NDT];
+  v16f acc_l[kSub];
 #pragma unroll
-  for (int d = 0; d < NDT; ++d) acc_o[d] = v16f{};
-  v16f acc_l = v16f{};
+  for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+    for (int d = 0; d < NDT; ++d) acc_o[sub][d] = v16f{};
+    acc_l[sub] = v16f{};
+  }
   const int u_off = SM::U_OFF + (li < 2 ? li : 2) * SM::VROW + 32 * hh;
   auto load_v = [&](const uint8_t* st, v8i (&vop)[NDT + 1]) {
 #pragma unroll
@@ -617,16 +632,15 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
                    (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
     }
   };
-  // product j of the NDT + 1: d sub-tile j, or the row sum (j = NDT)
-  // (P' of a tile carries rho relative to the tile's 2^e: the V products
-  // scale it back by the E8M0 exponent ev = 127 + e)
-  auto pv_step = [&](int j, const v8i (&vop)[NDT + 1], const v8i& pop, const v8i& plo, int ev) {
+  // product j of the NDT + 1 of one sub-tile: d sub-tile j, or the row sum (j = NDT)
+  v8i pop[kSub], plo[kSub];
+  auto pv_step = [&](int j, int sub, const v8i (&vop)[NDT + 1], int ev) {
     if (j < NDT) {
-      acc_o[j] = mfma_fp8_scaled(vop[j], pop, acc_o[j], 127, ev);
-      if constexpr (PLO) acc_o[j] = mfma_fp8_scaled(vop[j], plo, acc_o[j], 127, ev - kLoShift);
+      acc_o[sub][j] = mfma_fp8_scaled(vop[j], pop[sub], acc_o[sub][j], 127, ev);
+      if constexpr (PLO) acc_o[sub][j] = mfma_fp8_scaled(vop[j], plo[sub], acc_o[sub][j], 127, ev - kLoShift);
     } else {
-      acc_l = mfma_fp8_scaled(vop[NDT], pop, acc_l, 127 + 2, 127);
-      if constexpr (PLO) acc_l = mfma_fp8_scaled(vop[NDT], plo, acc_l, 127 + 2, 127 - kLoShift);
+      acc_l[sub] = mfma_fp8_scaled(vop[NDT], pop[sub], acc_l[sub], 127 + 2, 127);
+      if constexpr (PLO) acc_l[sub] = mfma_fp8_scaled(vop[NDT], plo[sub], acc_l[sub], 127 + 2, 127 - kLoShift);
     }
   };
 
@@ -651,22 +665,32 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
         make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  float m_run = -INFINITY;
-  v16f acc_s[2];
+  v16f acc_s[kSub][2];
+  float m_run[kSub];
   {
     v8i kop[2][NSTEP];
-    load_k(stage_of(0), kop, acc_s);
+    load_kop(stage_of(0), kop);
 #pragma unroll
-    for (int j = 0; j < 2 * NSTEP; ++j) qk_step(j, kop, acc_s);
+    for (int sub = 0; sub < kSub; ++sub) {
+      load_c(stage_of(0), acc_s[sub]);
+#pragma unroll
+      for (int j = 0; j < 2 * NSTEP; ++j) qk_step(j, sub, kop, acc_s[sub]);
+      if constexpr (MASK) mask_scores(0, acc_s[sub]);
+      // running max: from the raw row max of tile 0, so that the first tile
+      // leaves the same headroom as every rescale
+      float t0[32];
+      scores(acc_s[sub], (const float*)(stage_of(0) + SM::KF_OFF), hh, 0.0f, t0);
+      m_run[sub] = xhalf_max(max32(t0)) - (kLogPmax - kTau);
+      pop[sub] = v8i{};
+      plo[sub] = v8i{};
+    }
   }
-  if constexpr (MASK) mask_scores(0, acc_s);
-  v8i pop = v8i{}, plo = v8i{};
 
   // ---- main loop: iteration it computes the softmax of tile it while the
   // matrix cores take the PV product of tile it - 1 and the scores of tile
-  // it + 1; the ring holds tiles it - 1 .. it + 2
-  // one iteration; r = it mod 4 (a constant after the unrolling below), so
-  // that every LDS address is a lane base plus an immediate offset
+  // it + 1; the ring holds tiles it - 1 .. it + 2.  r = it mod 4 (a constant
+  // after the unrolling below), so that every LDS address is a lane base plus
+  // an immediate offset.
   auto tile_step = [&](const int it, const int r) __attribute__((always_inline)) {
     // (0) staging of tile it + 2 into the stage that tile it - 2 held (last
     // read before the previous barrier; first read of tile it + 2 after the
@@ -685,42 +709,54 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     v8i vop[NDT + 1];
     load_v(stage_of(r + 3), vop);
     const int ev = __builtin_amdgcn_readfirstlane(((const int*)(stage_of(r + 3) + SM::KF_OFF))[128]);
-    float t[32];
+    float t[kSub][32];
 #pragma unroll
     for (int c = 0; c < 4 || c <= NDT; ++c) {
-      // vector work first: the operand reads of the product land meanwhile
-      if (c < 4) {
 #pragma unroll
-        for (int w = 2 * c; w < 2 * c + 2; ++w) {
-          const float kk[4] = {kf4[w].x, kf4[w].y, kf4[w].z, kf4[w].w};
+      for (int sub = 0; sub < kSub; ++sub) {
+        // vector work first: the operand reads of the product land meanwhile
+        if (c < 4) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) t[4 * w + e] = __builtin_fmaf(acc_s[w >> 2][4 * (w & 3) + e], kk[e], -m_run);
+          for (int w = 2 * c; w < 2 * c + 2; ++w) {
+            const float kk[4] = {kf4[w].x, kf4[w].y, kf4[w].z, kf4[w].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              t[sub][4 * w + e] = __builtin_fmaf(acc_s[sub][w >> 2][4 * (w & 3) + e], kk[e], -m_run[sub]);
+          }
         }
+        if (c <= NDT) pv_step(c, sub, vop, ev);
       }
-      if (c <= NDT) pv_step(c, vop, pop, plo, ev);
       chunk_fence();
     }
-    // (any lane over the bound triggers: no cross-half max needed here)
-    const float mx = max32(t);
-    lazy_rescale<NDT>(acc_s, kf, hh, mx, m_run, acc_o, acc_l, t);
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) {
+      // (any lane over the bound triggers: no cross-half max needed here)
+      const float mx = max32(t[sub]);
+      lazy_rescale<NDT>(mx, m_run[sub], acc_o[sub], acc_l[sub], t[sub]);
+    }
 
     // (2) the score products of tile it + 1 (past the last tile they read a
-    // stale stage and are unused), interleaved with P' of tile it
+    // stale stage and are unused), interleaved with P' of tile it; one
+    // sub-tile after the other, so that few scores and products are live
     {
       v8i kop[2][NSTEP];
-      load_k(stage_of(r + 1), kop, acc_s);
+      load_kop(stage_of(r + 1), kop);
 #pragma unroll
-      for (int c = 0; c < 4 || c < 2 * NSTEP; ++c) {
-        if (c < 4) probs_quarter<PLO>(c, t, pop, plo);
-        if (c < 2 * NSTEP) qk_step(c, kop, acc_s);
-        chunk_fence();
+      for (int sub = 0; sub < kSub; ++sub) {
+        load_c(stage_of(r + 1), acc_s[sub]);
+#pragma unroll
+        for (int c = 0; c < 4 || c < 2 * NSTEP; ++c) {
+          if (c < 4) probs_quarter<PLO>(c, t[sub], pop[sub], plo[sub]);
+          if (c < 2 * NSTEP) qk_step(c, sub, kop, acc_s[sub]);
+          chunk_fence();
+        }
+        // keep the exponentials here rather than sunk past the staging
+        // branches towards their use in the next iteration
+        asm volatile("" ::"v"(pop[sub]));
+        if constexpr (PLO) asm volatile("" ::"v"(plo[sub]));
+        if constexpr (MASK) mask_scores(it + 1, acc_s[sub]);
       }
     }
-    // keep the exponentials here rather than sunk past the staging branches
-    // towards their use in the next iteration
-    asm volatile("" ::"v"(pop));
-    if constexpr (PLO) asm volatile("" ::"v"(plo));
-    if constexpr (MASK) mask_scores(it + 1, acc_s);
 
     __syncthreads();
   };
@@ -734,43 +770,49 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     load_v(stage_of(n_it - 1), vop);
     const int ev = __builtin_amdgcn_readfirstlane(((const int*)(stage_of(n_it - 1) + SM::KF_OFF))[128]);
 #pragma unroll
-    for (int j = 0; j <= NDT; ++j) pv_step(j, vop, pop, plo, ev);
+    for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+      for (int j = 0; j <= NDT; ++j) pv_step(j, sub, vop, ev);
   }
 
   // ---- epilogue ----------------------------------------------------------------
-  // row sum: rows 0 and 1 of L (registers 0 and 1 of the lanes hh = 0; the
-  // same registers of the lanes hh = 1 hold the zero rows 4 and 5)
-  const float l_tot = xhalf_sum(acc_l[0] + acc_l[1]);
-  if (part >= 0) {
-    // partial result of a key range: sum p V and sum p (p = 2^(score - m)),
-    // with m
-    const int q = wave * kQPW + li;
-    float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
-    const float inv_c = 1.0f / kPW;
 #pragma unroll
-    for (int d = 0; d < NDT; ++d)
+  for (int sub = 0; sub < kSub; ++sub) {
+    // row sum: rows 0 and 1 of L (registers 0 and 1 of the lanes hh = 0; the
+    // same registers of the lanes hh = 1 hold the zero rows 4 and 5)
+    const float l_tot = xhalf_sum(acc_l[sub][0] + acc_l[sub][1]);
+    const int row = q_rows[sub];
+    if (part >= 0) {
+      // partial result of a key range: sum p V and sum p (p = 2^(score - m)),
+      // with m
+      const int q = wave * kQPW + sub * 32 + li;
+      float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
+      const float inv_c = 1.0f / kPW;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * d + 8 * g + 4 * hh;
-        *(float4*)(po + d0) = make_float4(acc_o[d][4 * g + 0] * inv_c, acc_o[d][4 * g + 1] * inv_c,
-                                          acc_o[d][4 * g + 2] * inv_c, acc_o[d][4 * g + 3] * inv_c);
-      }
-    if (hh == 0) *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) = make_float2(m_run, l_tot / kPW);
-    return;
-  }
-  const float scale = 1.0f / l_tot;
-  if (q_row < a.n_tokens) {
-    uint16_t* dst = a.out + (int64_t)q_row * a.ldo + (int64_t)head * D;
+      for (int d = 0; d < NDT; ++d)
 #pragma unroll
-    for (int d = 0; d < NDT; ++d)
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * d + 8 * g + 4 * hh;
+          *(float4*)(po + d0) = make_float4(acc_o[sub][d][4 * g + 0] * inv_c, acc_o[sub][d][4 * g + 1] * inv_c,
+                                            acc_o[sub][d][4 * g + 2] * inv_c, acc_o[sub][d][4 * g + 3] * inv_c);
+        }
+      if (hh == 0) *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) = make_float2(m_run[sub], l_tot / kPW);
+      continue;
+    }
+    const float scale = 1.0f / l_tot;
+    if (row < a.n_tokens) {
+      uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * d + 8 * g + 4 * hh;
-        uint2 w;
-        w.x = pack_bf16x2(acc_o[d][4 * g + 0] * scale, acc_o[d][4 * g + 1] * scale);
-        w.y = pack_bf16x2(acc_o[d][4 * g + 2] * scale, acc_o[d][4 * g + 3] * scale);
-        *(uint2*)(dst + d0) = w;
-      }
+      for (int d = 0; d < NDT; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * d + 8 * g + 4 * hh;
+          uint2 w;
+          w.x = pack_bf16x2(acc_o[sub][d][4 * g + 0] * scale, acc_o[sub][d][4 * g + 1] * scale);
+          w.y = pack_bf16x2(acc_o[sub][d][4 * g + 2] * scale, acc_o[sub][d][4 * g + 3] * scale);
+          *(uint2*)(dst + d0) = w;
+        }
+    }
   }
 }
 
