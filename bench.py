@@ -299,7 +299,7 @@ def main():
     att_traffic = traffic_of(args.traffic_json, "attend_kernel<128, false, false, false>")
     comb_traffic = traffic_of(args.traffic_json, "combine_kernel<128>")
     fac_traffic = traffic_of(args.traffic_json, "factors_kernel")
-    app_traffic = traffic_of(args.traffic_json, "append_rope_quant_kernel<128>")
+    app_traffic = traffic_of(args.traffic_json, "append_rope_quant_kernel<128")
     traffic = None
     if att_traffic:
         traffic = sum(v["bytes"] for v in att_traffic.values())
@@ -338,7 +338,7 @@ def main():
             "flops_per_launch_full_window": algorithmic(wl, wl.capacity_frames)[1],
         },
         "append_roofline": {
-            "bound": "hbm", "kernel": "append_rope_quant_kernel<128>",
+            "bound": "hbm", "kernel": "append_rope_quant_kernel<128, 3> (3 KV heads per workgroup)",
             "achieved": round(app_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(app_gbs / HBM_PEAK_GBS, 4), "avg_launch_ms": round(app_avg_ms, 5),
             "bytes_per_launch": app_bytes, "traffic": app_bytes_measured,
