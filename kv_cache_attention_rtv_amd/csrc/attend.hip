@@ -29,10 +29,16 @@
 // the key's 64-slot tile; the PV product scales P' back by 2^e through the
 // E8M0 scale of its B operand (exact), so that it sums 55 p sv Vcodes.
 // log2(55 rho) enters as the accumulator's initial value
-// C = log2(55 rho) / kf, so t = fma(S, kf, -m) = log2 P' and P' is one exp2
-// and one conversion per score.  The row sum is taken from the same e4m3 P'
-// by the matrix cores, against U = 1/rho as two e4m3 terms (rows 0 and 1 of
-// U): numerator and denominator share the rounding of P'.  The per-key
+// C = log2(55 rho) / kf, so t = fma(S, kf, -m) = log2 P' and P' costs one
+// FMA and one conversion per score.  Long windows take the e4m3 code of P'
+// straight from t: with kf and m in units of 1/8 octave the FMA gives
+// u = 8 t + 56, and v_cvt_pk_u8_f32 rounds u to the nearest integer and
+// saturates it to [0, 255], which is the code of the e4m3 value whose
+// piecewise-linear log2 (exponent + mantissa / 8) lies nearest to t (within
+// one code of the RNE e4m3 of 2^t; no exponential).  Short windows take
+// 2^t with v_exp_f32 and carry it as two e4m3 terms.  The row sum is taken
+// from the same e4m3 P' by the matrix cores, against U = 1/rho as two e4m3
+// terms (rows 0 and 1 of U): numerator and denominator share P'.  The per-key
 // factors come from a small factors kernel run before the attention.  The
 // running max m is lazy: it moves only when some P' would exceed 440, and
 // then leaves a factor 2^kTau of headroom.  Output O = acc / L, rounded to
@@ -60,6 +66,15 @@ constexpr int kSub = kQPW / 32;             // 32-query sub-tiles per wave (they
 constexpr int kStages = 4;                  // LDS ring: tiles it - 1 .. it + 2
 constexpr float kTau = 3.0f;
 constexpr float kLogPmax = 8.78135971f;     // log2(440): bound on P' (below the e4m3 max 448)
+// log-domain units of the scores: u = kUnit * log2 P' + kOff.  Exact path
+// (two-term P' from v_exp_f32): u = t.  Linear-code path: u = 8 t + 56 is the
+// e4m3 code of P' before rounding (code 8 e + m <-> 2^(e - 7) (1 + m / 8)).
+template <bool EXACT> struct LogUnits {
+  static constexpr float kUnit = EXACT ? 1.0f : 8.0f;
+  static constexpr float kOff = EXACT ? 0.0f : 56.0f;
+  static constexpr float kTop = kUnit * kLogPmax + kOff;    // u bound: P' <= 440
+  static constexpr float kReset = kTop - kUnit * kTau;      // largest u after a rescale
+};
 constexpr float kPW = 55.0f;                // P' = p * kPW * rho, rho <= 1
 constexpr float kLogPW = 5.78135971f;       // log2(kPW)
 constexpr float kRhoMin = 0.0009765625f;    // 2^-10: floor of rho (U = 2^-2 / rho <= 256)
@@ -144,13 +159,29 @@ struct TileRef {
 // dword 3 of a raw buffer descriptor (32-bit elements, no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 
+// Byte offset in a 64-slot tile of the first of the D/64 adjacent 16-byte
+// pieces of codes that thread g (0..255) of a side moves.  The 16 lanes of
+// each quarter wave take 16 different rows at one column, as the operand
+// reads do, so that the padded LDS rows spread their writes over the banks.
+// K: 64 rows of D bytes, 4 threads per row, 16 rows per wave.
+template <int D>
+__device__ __forceinline__ int k_code_off(int g) {
+  return (16 * (g >> 6) + (g & 15)) * D + ((g >> 4) & 3) * (D / 4);
+}
+// transposed V: D rows of 64 bytes, 256 / D threads per row
+template <int D>
+__device__ __forceinline__ int v_code_off(int g) {
+  constexpr int RPW = 64 / (256 / D);       // rows per wave
+  return (RPW * (g >> 6) + (g % RPW)) * 64 + ((g & 63) / RPW) * (D / 4);
+}
+
 // The side (K or V) of a thread is uniform over its wave (side = -1 for
 // 256-thread workgroups, where every thread does both); the addresses are a
 // wave-uniform base plus a per-lane offset that does not change with the tile.
 template <int D>
 __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const uint8_t* kc,
                                           const uint8_t* vc, const uint8_t* frec, const uint8_t* fu,
-                                          int side, int code_off, int xk_off, int xv_off) {
+                                          int side, int k_off, int v_off, int xk_off, int xv_off) {
   constexpr int LD_BYTES = D / 4;
 #pragma unroll
   for (int j = 0; j < kStageJobs; ++j) {
@@ -158,6 +189,7 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const TileRef& t, const u
     // buffer loads through a descriptor of exactly this tile's bytes
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((isv ? vc : kc) + (int64_t)t.tile * 64 * D), 0, 64 * D, kBufferFlags);
+    const int code_off = isv ? v_off : k_off;
     r.c[j][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, code_off, 0, 0));
     if constexpr (LD_BYTES == 32)
       r.c[j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, code_off + 16, 0, 0));
@@ -209,11 +241,11 @@ __device__ __forceinline__ int vt_pos(int k) {
   return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);
 }
 
-// kscale = max(s_q * log2(e) / sqrt(D), kScaleMin), inv_kscale = 1 / kscale.
+// kscale = kUnit * max(s_q * log2(e) / sqrt(D), kScaleMin) (kf in the score
+// units), inv_kscale = 1 / max(s_q * log2(e) / sqrt(D), kScaleMin).
 // The codes are stored branch-free apart from the masking of partial tiles:
-// K and V pieces differ only in their address.  The K side writes kf and C of
-// key (thread & 63), the V side the U rows; threads that share a key or a
-// piece write the same values.
+// K and V pieces differ only in their address.  The first K-side wave writes
+// kf and C (lane = key), lanes 0..7 of the first V-side wave the U rows.
 template <int D, bool MASK>
 __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, uint8_t* st,
                                            float kscale, float inv_kscale, int tid) {
@@ -222,10 +254,10 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, 
   const int gt = tid & 255;
   const int base = t.tile * 64;
   const bool partial = MASK && (t.lo > base || t.hi < base + 64);
-  const int b = gt * LD_BYTES;
 #pragma unroll
   for (int j = 0; j < kStageJobs; ++j) {
     const bool isv = kStageJobs == 1 ? tid >= 256 : j == 1;
+    const int b = isv ? v_code_off<D>(gt) : k_code_off<D>(gt);
 #pragma unroll
     for (int h = 0; h < LD_BYTES / 16; ++h) {
       const int bb = b + 16 * h;
@@ -234,15 +266,17 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, 
       *(uint4*)(st + (isv ? v_piece_at<D>(bb) : k_piece_at<D>(bb))) = q;
     }
   }
-  const bool kside = kStageJobs == 2 || __builtin_amdgcn_readfirstlane(tid) < 256;
-  const bool vside = kStageJobs == 2 || !kside;
+  const int wave = __builtin_amdgcn_readfirstlane(tid) >> 6;
+  const bool kside = wave == 0;
+  const bool vside = wave == (kStageJobs == 2 ? 0 : 4) && (tid & 63) < 8;
   const uint4 xk = r.x[0];
   const uint4 xv = r.x[kStageJobs - 1];
   if (kside) {
-    // t = (S + C) * kf - m = S * kf + log2(55 rho) - m.  A key outside the
-    // segment gets kf = kMaskFactor and C = 0: its raw score is the bias
-    // -448*448 added by the masking MFMA, so t ~ -2e35 and P' = 0
-    const int key = gt & 63;
+    // u = (S + C) * kf - m = kUnit (S * kf1 + log2(55 rho)) - m with kf1 the
+    // factor in log2 units.  A key outside the segment gets kf = kMaskFactor
+    // and C = 0: its raw score is the bias -448*448 added by the masking MFMA,
+    // so u ~ -2e35 and P' = 0
+    const int key = tid & 63;
     const bool ok = !MASK || (base + key >= t.lo && base + key < t.hi);
     const float kf = __uint_as_float(xk.x) * kscale;
     const float c = __uint_as_float(xk.y) * inv_kscale;
@@ -252,7 +286,7 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, 
     if (key == 0) ((uint32_t*)kfp)[128] = xk.z;
   }
   if (vside) {
-    const int piece = gt & 7;
+    const int piece = tid & 7;
     *(uint4*)(st + SM::U_OFF + (piece >> 2) * SM::VROW + 16 * (piece & 3)) = xv;
   }
 }
@@ -343,18 +377,19 @@ __device__ __forceinline__ float max32(const float (&t)[32]) {
 }
 
 // Softmax of one 32-query tile over one 64-key tile, first half (after
-// t = fma(S, kf, -m), mx = the lane's max of t): the lazy running-max update.
-// Rare: only when some P' would exceed 440; it rescales the O and row-sum
-// accumulators, shifts t and leaves the largest P' of the row at 440 / 2^kTau.
-// m is finite from the first tile on (set from tile 0 before the loop), so
-// the raw row max is max(t) + m and no score is recomputed.
-template <int NDT>
+// u = fma(S, kf, -m), mx = the lane's max of u, all in the units of LU): the
+// lazy running-max update.  Rare: only when some P' would exceed 440; it
+// rescales the O and row-sum accumulators, shifts u and leaves the largest
+// P' of the row at 440 / 2^kTau.  m is finite from the first tile on (set
+// from tile 0 before the loop), so the raw row max is max(u) + m and no
+// score is recomputed.
+template <int NDT, class LU>
 __device__ __forceinline__ void lazy_rescale(float mx, float& m, v16f (&o)[NDT], v16f& lsum, float (&t)[32]) {
-  if (__builtin_expect(__any(mx > kLogPmax), 0)) {
+  if (__builtin_expect(__any(mx > LU::kTop), 0)) {
     const float raw = xhalf_max(mx) + m;
-    const float m_new = __builtin_fmaxf(m, raw - (kLogPmax - kTau));
+    const float m_new = __builtin_fmaxf(m, raw - LU::kReset);
     const float shift = m - m_new;
-    const float alpha = exp2f(shift);
+    const float alpha = exp2f(shift * (1.0f / LU::kUnit));
 #pragma unroll
     for (int d = 0; d < NDT; ++d) o[d] *= alpha;
     lsum *= alpha;
@@ -364,28 +399,32 @@ __device__ __forceinline__ void lazy_rescale(float mx, float& m, v16f (&o)[NDT],
   }
 }
 
-// Second half, in quarters (keys 8c .. 8c + 7 of the lane): P' = 2^t in e4m3,
-// the B operand of the PV and row-sum products (PRECISE: as two terms).
+// Second half, in quarters (keys 8c .. 8c + 7 of the lane): P' in e4m3, the
+// B operand of the PV and row-sum products.  PRECISE: 2^t as two terms;
+// otherwise the code is u = 8 t + 56 rounded and saturated to [0, 255] (u
+// stays below 126.5 by the running max, so codes reach at most 0x7E = 448; a
+// key far below the max, or masked, gives +0).
 template <bool PRECISE>
 __device__ __forceinline__ void probs_quarter(int c, const float (&t)[32], v8i& pop, v8i& plo) {
 #pragma unroll
   for (int w = 2 * c; w < 2 * c + 2; ++w) {
-    float pp[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pp[e] = __builtin_amdgcn_exp2f(t[4 * w + e]);
     if constexpr (PRECISE) {
+      float pp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pp[e] = __builtin_amdgcn_exp2f(t[4 * w + e]);
       uint32_t hi = 0, lo = 0;
       split_fp8x2<false>(pp[0], pp[1], hi, lo);
       split_fp8x2<true>(pp[2], pp[3], hi, lo);
       pop[w] = (int)hi;
       plo[w] = (int)lo;
     } else {
-      // the low half is written first and the high half next, so the old
-      // contents of the register do not matter: pp[0], dead after this
-      // instruction, is that register
-      uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], __float_as_int(pp[0]), false);
-      hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], (int)hi, true);
-      pop[w] = (int)hi;
+      // bytes 0..3 in turn: every byte of the register is written, so its
+      // old contents (t[4 w], dead after the first conversion) do not matter
+      uint32_t x = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * w + 0], 0, __float_as_uint(t[4 * w + 0]));
+      x = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * w + 1], 1, x);
+      x = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * w + 2], 2, x);
+      x = __builtin_amdgcn_cvt_pk_u8_f32(t[4 * w + 3], 3, x);
+      pop[w] = (int)x;
     }
   }
 }
@@ -408,6 +447,7 @@ __device__ __forceinline__ void chunk_fence() { __builtin_amdgcn_sched_barrier(0
 template <int D, bool MASK, bool QLO, bool PLO>
 __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(AttendArgs a) {
   using SM = Smem<D>;
+  using LU = LogUnits<PLO>;
   constexpr int NSTEP = D / 64;             // MFMA k-steps for K.Q^T
   constexpr int NDT = D / 32;               // 32-row d sub-tiles of O^T
   constexpr int P = D / 4;                  // RoPE pairs per lane
@@ -443,7 +483,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   const uint8_t* frec = (const uint8_t*)a.fac_l + (int64_t)kvh * a.ring_tiles * 1024;
   const uint8_t* fu = a.fac_u + (int64_t)kvh * a.ring_tiles * 128;
   const int side = kStageJobs == 1 ? (__builtin_amdgcn_readfirstlane(tid) >= 256 ? 1 : 0) : -1;
-  const int code_off = (tid & 255) * (D / 4);
+  const int k_off = k_code_off<D>(tid & 255), v_off = v_code_off<D>(tid & 255);
   const int xk_off = (tid & 63) * 16, xv_off = (tid & 7) * 16;
 
   // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
@@ -483,6 +523,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   const float q_inv = qamax > 0.0f ? kFp8Max / qamax : 0.0f;
   const float kscale = __builtin_fmaxf((qamax / kFp8Max) * (kLog2e / sqrtf((float)D)), kScaleMin);
   const float inv_kscale = 1.0f / kscale;
+  const float kscale_u = kscale * LU::kUnit;  // kf in the score units (C stays in raw units)
 
   // ---- Q prologue pass 2: e4m3 codes in the B-operand layout ---------------
   // operand step s, byte b <-> d: D=128: d = 64 s + 32 hh + b; D=64: byte b < 16
@@ -652,10 +693,10 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   if (n_it > 0) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      load_tile<D>(regs, tref(clamp_it(p)), kc, vc, frec, fu, side, code_off, xk_off, xv_off);
-      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale, inv_kscale, tid);
+      load_tile<D>(regs, tref(clamp_it(p)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
+      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale_u, inv_kscale, tid);
     }
-    load_tile<D>(regs, tref(clamp_it(2)), kc, vc, frec, fu, side, code_off, xk_off, xv_off);
+    load_tile<D>(regs, tref(clamp_it(2)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
   }
   for (int i = tid; i < SM::V_BYTES / 16; i += kThreads)
     ((uint4*)(stage_of(-1) + SM::K_BYTES))[i] = make_uint4(0, 0, 0, 0);
@@ -680,7 +721,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
       // leaves the same headroom as every rescale
       float t0[32];
       scores(acc_s[sub], (const float*)(stage_of(0) + SM::KF_OFF), hh, 0.0f, t0);
-      m_run[sub] = xhalf_max(max32(t0)) - (kLogPmax - kTau);
+      m_run[sub] = xhalf_max(max32(t0)) - LU::kReset;
       pop[sub] = v8i{};
       plo[sub] = v8i{};
     }
@@ -697,8 +738,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     // next one) and the loads of tile it + 3; at the top of the iteration so
     // that its latency overlaps the products.  Unconditional with the tile
     // index clamped: past the end the copy lands in a stage nobody reads again
-    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(r + 2), kscale, inv_kscale, tid);
-    load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, frec, fu, side, code_off, xk_off, xv_off);
+    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(r + 2), kscale_u, inv_kscale, tid);
+    load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
 
     // (1) the PV and row-sum products of tile it - 1, interleaved with the
     // scores of tile it: t = fma(S, kf, -m), a quarter (8 keys) per product
@@ -732,7 +773,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     for (int sub = 0; sub < kSub; ++sub) {
       // (any lane over the bound triggers: no cross-half max needed here)
       const float mx = max32(t[sub]);
-      lazy_rescale<NDT>(mx, m_run[sub], acc_o[sub], acc_l[sub], t[sub]);
+      lazy_rescale<NDT, LU>(mx, m_run[sub], acc_o[sub], acc_l[sub], t[sub]);
     }
 
     // (2) the score products of tile it + 1 (past the last tile they read a
@@ -796,7 +837,10 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
           *(float4*)(po + d0) = make_float4(acc_o[sub][d][4 * g + 0] * inv_c, acc_o[sub][d][4 * g + 1] * inv_c,
                                             acc_o[sub][d][4 * g + 2] * inv_c, acc_o[sub][d][4 * g + 3] * inv_c);
         }
-      if (hh == 0) *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) = make_float2(m_run[sub], l_tot / kPW);
+      // (m back in log2 units: u = kUnit t + kOff with m_u = kUnit m - kOff)
+      if (hh == 0)
+        *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) =
+            make_float2((m_run[sub] + LU::kOff) * (1.0f / LU::kUnit), l_tot / kPW);
       continue;
     }
     const float scale = 1.0f / l_tot;
