@@ -111,8 +111,9 @@ typedef struct rtv_window {
 /* ---- sizing and lifetime ------------------------------------------------ */
 
 /* Device bytes the caller must provide to rtv_cache_create for `cfg`:
- * the RoPE table (max_global_frames*T positions x D/2 (cos, sin) f32 pairs)
- * plus, per layer, the codes and scales above.  Host-only; no GPU needed. */
+ * the RoPE table (max_global_frames*T positions x D/2 (cos, sin) f32 pairs),
+ * the attention workspace, 16 bytes of ring state per layer (device-state
+ * mode) and, per layer, the codes and scales above.  Host-only; no GPU needed. */
 rtv_status rtv_cache_bytes(const rtv_config* cfg, size_t* bytes);
 
 /* Create a cache handle over the caller's device buffer `dev_buf` (>= the
@@ -169,8 +170,38 @@ rtv_status rtv_attend(rtv_cache* cache, int32_t layer,
 
 /* Commit the current chunk of `layer` (-1 = every layer): the head index moves
  * by chunk_frames, committed = min(committed + F, C).  Host state only; no
- * device work is enqueued.  Errors: STATE (no append since the last advance). */
+ * device work is enqueued (in the device-state mode below: one small kernel on
+ * `stream` that moves the state in the arena).  Errors: STATE (no append since
+ * the last advance). */
 rtv_status rtv_advance(rtv_cache* cache, int32_t layer, void* stream);
+
+/* ---- device-resident ring state (for graph capture) ----------------------
+ * The pages capture the forward pass in a CUDA graph [page "Runway partage la
+ * construction de Runway Characters" (lhc.media), fourth paragraph].  A
+ * captured graph freezes kernel arguments, while the ring state moves every
+ * step.  Between rtv_device_state_begin and rtv_device_state_end the state of
+ * every layer (next global frame, committed frames) lives in the arena:
+ *   - rtv_append_rope_quant and rtv_attend enqueue kernels that read it (the
+ *     chunk's slots, its RoPE rows, the window, the split schedule), with
+ *     grids sized for the largest window;
+ *   - rtv_advance enqueues a kernel that moves it;
+ * so a sequence of these calls captured once (hipStreamBeginCapture, or
+ * torch.cuda.graph) replays correctly step after step.  The results equal
+ * the host-state calls' (same kernels and arithmetic), with one difference in
+ * the variant: windows shorter than 8192 keys carry Q and P' as two e4m3
+ * terms, and in this mode the choice follows the shortest possible window
+ * (one chunk) instead of the current one.
+ * While the mode is on, rtv_cache_layout and rtv_cache_window report the
+ * state as of rtv_device_state_begin, and the host checks only the argument
+ * and call-order rules; a chunk past the end of the RoPE table makes the
+ * kernels write nothing and is reported by rtv_device_state_end.
+ * rtv_device_state_begin copies the host state into the arena and
+ * synchronizes `stream`.  Errors: STATE (already on), HIP. */
+rtv_status rtv_device_state_begin(rtv_cache* cache, void* stream);
+/* Copy the state back to the host (synchronizes `stream`) and return to the
+ * host-state mode.  Errors: STATE (the mode was off, or a call in the mode
+ * found the RoPE table exhausted; the state is copied back either way), HIP. */
+rtv_status rtv_device_state_end(rtv_cache* cache, void* stream);
 
 /* ---- inspection (tests, fused producers) -------------------------------- */
 

@@ -83,6 +83,8 @@ def _load():
         "rtv_append_rope_quant": (I32, [P, I32, P, I64, P, I64, I32, P]),
         "rtv_attend": (I32, [P, I32, P, I64, P, I64, I32, P]),
         "rtv_advance": (I32, [P, I32, P]),
+        "rtv_device_state_begin": (I32, [P, P]),
+        "rtv_device_state_end": (I32, [P, P]),
         "rtv_cache_layout": (I32, [P, I32, ctypes.POINTER(rtv_layout)]),
         "rtv_cache_window": (I32, [P, I32, I32, ctypes.POINTER(rtv_window)]),
         "rtv_ring_window": (I32, [I64, I32, I32, I32, I32, I32, ctypes.POINTER(rtv_window)]),
@@ -109,7 +111,7 @@ def _load():
 lib = _load()
 EXPORTED = (
     "rtv_cache_bytes", "rtv_cache_create", "rtv_destroy", "rtv_append_rope_quant",
-    "rtv_attend", "rtv_advance", "rtv_cache_layout", "rtv_cache_window", "rtv_ring_window",
+    "rtv_attend", "rtv_advance", "rtv_device_state_begin", "rtv_device_state_end", "rtv_cache_layout", "rtv_cache_window", "rtv_ring_window",
     "rtv_rope_fill_host", "rtv_encode_e4m3", "rtv_status_string",
     "rtv_quant_workspace_bytes", "rtv_quant_fp8_per_tensor", "rtv_gemm_fp8",
 )
@@ -154,6 +156,14 @@ def rtv_attend(handle, layer, q_ptr, q_stride, out_ptr, out_stride, max_window_f
 
 def rtv_advance(handle, layer, stream):
     check(lib.rtv_advance(handle, layer, stream), "rtv_advance")
+
+
+def rtv_device_state_begin(handle, stream):
+    check(lib.rtv_device_state_begin(handle, stream), "rtv_device_state_begin")
+
+
+def rtv_device_state_end(handle, stream):
+    check(lib.rtv_device_state_end(handle, stream), "rtv_device_state_end")
 
 
 def rtv_cache_layout(handle, layer) -> rtv_layout:

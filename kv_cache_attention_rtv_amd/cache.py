@@ -94,6 +94,19 @@ class RtvCache:
     def advance(self, layer: int = -1, stream=None):
         abi.rtv_advance(self.handle, layer, _stream(stream))
 
+    # -- device-resident ring state (graph capture) -------------------------
+    def device_state_begin(self, stream=None):
+        """Move the ring state of every layer into device memory: append, attend
+        and advance then read and move it in their kernels, so that a captured
+        sequence of them replays correctly step after step.  Synchronizes."""
+        abi.rtv_device_state_begin(self.handle, _stream(stream))
+
+    def device_state_end(self, stream=None):
+        """Copy the ring state back to the host and leave the device-state mode.
+        Synchronizes; raises RtvError(RTV_ERR_STATE) if a call in the mode ran
+        past the RoPE table (its kernels wrote nothing)."""
+        abi.rtv_device_state_end(self.handle, _stream(stream))
+
     # -- inspection ----------------------------------------------------------
     def layout(self, layer: int) -> abi.rtv_layout:
         return abi.rtv_cache_layout(self.handle, layer)

@@ -23,6 +23,7 @@
 // quotient (div_rn), and the e4m3 conversion rounds to nearest even.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "ring.hpp"
 
 namespace rtv {
 namespace {
@@ -85,6 +86,29 @@ __device__ __forceinline__ RowPiece<D / 16> load_piece(const uint16_t* row, int 
   return r;
 }
 
+// Device-state mode: the chunk's first slot and RoPE rows from the layer's
+// ring state (the host computes the same from its copy in host-state mode).
+// False, with the state's error set, when the chunk would run past the RoPE
+// table: the kernel then writes nothing.
+template <int D>
+__device__ __forceinline__ bool append_derive(AppendArgs& a, int groups) {
+  const RingShape& g = a.shape;
+  const int64_t next = a.dstate->next_global_frame;
+  RingWindow w;
+  if (next + g.chunk_frames > g.max_global_frames ||
+      ring_window(next, a.dstate->committed, g.tokens_per_frame, g.chunk_frames, g.capacity_frames, 0, &w) !=
+          kRingOk) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.dstate->error = 1;
+    return false;
+  }
+  a.write_slot = w.write_slot;
+  a.rope = a.rope_table + next * g.tokens_per_frame * D;
+  a.first_tile = (int32_t)(w.write_slot / kTileKeys);
+  const int64_t last_tile = (w.write_slot + a.n_tokens - 1) / kTileKeys;
+  a.n_work = (int32_t)(last_tile - a.first_tile + 1) * groups;
+  return true;
+}
+
 template <int D, int HPW>
 __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(AppendArgs a) {
   constexpr int E = D / 16;          // elements per lane per half
@@ -94,6 +118,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
   __shared__ uint32_t vrow[HPW][kTileKeys * LDS_STRIDE / 4];
 
   const int groups = (a.n_heads + HPW - 1) / HPW;
+  if (a.dstate && !append_derive<D>(a, groups)) return;
   const int u = xcd_remap(blockIdx.x, a.n_work);
   if (u < 0) return;
   const int st = a.first_tile + u / groups;
@@ -273,6 +298,21 @@ hipError_t launch_append(const AppendArgs& args_in, int head_dim, hipStream_t st
   else
     hipLaunchKernelGGL((append_rope_quant_kernel<64, kAppendHeads>), dim3(blocks), dim3(kAppendThreads), 0,
                        stream, args);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(64) void advance_kernel(DevRingState* s, int n, int chunk_frames, int capacity_frames) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    s[i].next_global_frame += chunk_frames;
+    const int c = s[i].committed + chunk_frames;
+    s[i].committed = c < capacity_frames ? c : capacity_frames;
+  }
+}
+
+hipError_t launch_advance(DevRingState* s, int n, int chunk_frames, int capacity_frames, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(advance_kernel, dim3((n + 63) / 64), dim3(64), 0, stream, s, n, chunk_frames, capacity_frames);
   return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@
 // bf16.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "ring.hpp"
 
 namespace rtv {
 namespace {
@@ -102,6 +103,8 @@ __device__ __forceinline__ v16f mfma_fp8_scaled(const v8i& a, const v8i& b, cons
 constexpr int kLoShift = 4;
 // windows shorter than this many keys also carry P' as two terms (PLO)
 constexpr int64_t kPreciseKeys = 8192;
+// split-key-range parts are bounded so that the workspace has a fixed size
+constexpr int kMaxParts = 512;
 template <bool HIGH>
 __device__ __forceinline__ void split_fp8x2(float a, float b, uint32_t& hi, uint32_t& lo) {
   constexpr float kLoMul = (float)(1 << kLoShift);
@@ -308,7 +311,33 @@ __device__ __forceinline__ TileRef tile_of(int it, int t_count0, int t_first0, i
 // two e4m3 terms of 2^-2 / rho at the slot's byte position in the U rows.
 // Slots of a partial tile outside the window get factors too (from whatever
 // their scales hold; the attention masks them).
+// Device-state mode: the window's segments, the chunk's RoPE rows and the
+// split schedule from the layer's ring state, with the same arithmetic as the
+// host's in host-state mode.  False, with the state's error set, when the
+// chunk would run past the RoPE table or the state is not a ring state: the
+// call's kernels then write nothing.
+__device__ __forceinline__ bool attend_derive(AttendArgs& a) {
+  const RingShape& g = a.shape;
+  const int64_t next = a.dstate->next_global_frame;
+  RingWindow w;
+  if (next + g.chunk_frames > g.max_global_frames ||
+      ring_window(next, a.dstate->committed, g.tokens_per_frame, g.chunk_frames, g.capacity_frames,
+                  g.max_window_frames, &w) != kRingOk) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.dstate->error = 1;
+    return false;
+  }
+  a.rope = a.rope_table + next * g.tokens_per_frame * g.head_dim;
+  a.n_segments = w.n_segments;
+  a.seg_lo[0] = w.seg_start[0];
+  a.seg_hi[0] = w.seg_start[0] + w.seg_len[0];
+  a.seg_lo[1] = w.seg_start[1];
+  a.seg_hi[1] = w.seg_start[1] + w.seg_len[1];
+  attend_schedule(a, attend_window_tiles(a), kMaxParts);
+  return true;
+}
+
 __global__ __launch_bounds__(256) void factors_kernel(AttendArgs a) {
+  if (a.dstate && !attend_derive(a)) return;
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lo0 = (int)a.seg_lo[0], hi0 = (int)a.seg_hi[0];
@@ -446,6 +475,7 @@ __device__ __forceinline__ void chunk_fence() { __builtin_amdgcn_sched_barrier(0
 // cache was created for two query terms (keys with outlier channels).
 template <int D, bool MASK, bool QLO, bool PLO>
 __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(AttendArgs a) {
+  if (a.dstate && !attend_derive(a)) return;
   using SM = Smem<D>;
   using LU = LogUnits<PLO>;
   constexpr int NSTEP = D / 64;             // MFMA k-steps for K.Q^T
@@ -864,7 +894,9 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
 // M = max_p m_p, w_p = 2^(m_p - M), O = sum_p w_p O_p / sum_p w_p l_p.
 template <int D>
 __global__ __launch_bounds__(2 * kQPB) void combine_kernel(AttendArgs a) {
+  if (a.dstate && !attend_derive(a)) return;
   const int r = blockIdx.x;                       // split unit r
+  if (a.n_full + r >= a.n_work) return;           // (device-state grids cover the most split units)
   const int unit = a.n_full + r;
   const int head = unit / a.n_qtiles;
   const int qtile = unit % a.n_qtiles;
@@ -908,8 +940,6 @@ __global__ __launch_bounds__(2 * kQPB) void combine_kernel(AttendArgs a) {
 
 int attend_queries_per_block() { return kQPB; }
 
-// parts are bounded so that the workspace has a fixed size
-constexpr int kMaxParts = 512;
 int attend_max_parts() { return kMaxParts; }
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 static size_t partials_bytes(int head_dim) {
@@ -947,38 +977,42 @@ hipError_t attend_capacity(int* workgroups) {
 
 hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t stream) {
   AttendArgs args = args_in;
-  bool aligned = true;
-  int64_t keys = 0;
-  int n_tiles = 0;
-  for (int s = 0; s < args.n_segments; ++s) {
-    aligned = aligned && args.seg_lo[s] % 64 == 0 && args.seg_hi[s] % 64 == 0;
-    keys += args.seg_hi[s] - args.seg_lo[s];
-    if (args.seg_hi[s] > args.seg_lo[s])
-      n_tiles += (int)((args.seg_hi[s] - 1) / 64 - args.seg_lo[s] / 64 + 1);
+  bool aligned = true, short_window = false;
+  int n_tiles = 0, grid_per_xcd = 0, rem = 0;
+  if (!args.dstate) {
+    int64_t keys = 0;
+    for (int s = 0; s < args.n_segments; ++s) {
+      aligned = aligned && args.seg_lo[s] % 64 == 0 && args.seg_hi[s] % 64 == 0;
+      keys += args.seg_hi[s] - args.seg_lo[s];
+    }
+    n_tiles = attend_window_tiles(args);
+    short_window = keys < kPreciseKeys;
+    attend_schedule(args, n_tiles, kMaxParts);
+    grid_per_xcd = args.full_per_xcd + args.parts_per_xcd;
+    rem = args.n_work - args.n_full;
+  } else {
+    // Device-state mode: the kernels derive the window and the schedule, so
+    // the variant and the grids are fixed by the ring's shape.  Every window
+    // holds at least one chunk and starts on a chunk boundary when the cap
+    // is a multiple of the chunk; the grids cover the largest window.
+    const RingShape& sh = args.shape;
+    const int64_t chunk = (int64_t)sh.chunk_frames * sh.tokens_per_frame;
+    aligned = chunk % 64 == 0 && sh.max_window_frames % sh.chunk_frames == 0;
+    short_window = chunk < kPreciseKeys;
+    n_tiles = (int)(((int64_t)sh.capacity_frames * sh.tokens_per_frame + 63) / 64) + 1;
+    AttendArgs whole = args, most = args;
+    attend_schedule(whole, 1, kMaxParts);
+    attend_schedule(most, n_tiles, kMaxParts);
+    const int g1 = whole.full_per_xcd + whole.parts_per_xcd, g2 = most.full_per_xcd + most.parts_per_xcd;
+    grid_per_xcd = g1 > g2 ? g1 : g2;
+    rem = most.n_work - most.n_full;
   }
-  const bool short_window = keys < kPreciseKeys;
   const bool two_term_q = short_window || args.two_term_q;
-
-  // Schedule: whole rounds of the device's concurrent workgroups run whole
-  // windows; the remainder, which would leave most of the device idle in a
-  // last round, is split along the keys so that it fills one short round.
-  const int cap = args.capacity;
-  const int U = args.n_work;
-  int rem = cap > 0 ? U % cap : 0;
-  int S = rem > 0 ? cap / rem : 1;
-  if (S > n_tiles) S = n_tiles;
-  if ((int64_t)rem * S > kMaxParts) S = kMaxParts / (rem > 0 ? rem : 1);
-  if (S < 2 || !args.ws_o) { S = 1; rem = 0; }
-  args.n_full = U - rem;
-  args.parts_per_unit = S;
-  args.n_parts = rem * S;
-  args.full_per_xcd = (args.n_full + 7) / 8;
-  args.parts_per_xcd = (args.n_parts + 7) / 8;
   {
     const int waves = n_tiles * args.n_kv_heads;
     if (waves > 0) hipLaunchKernelGGL(factors_kernel, dim3((waves + 3) / 4), dim3(256), 0, stream, args);
   }
-  const dim3 g(8 * (args.full_per_xcd + args.parts_per_xcd)), b(kThreads);
+  const dim3 g(8 * grid_per_xcd), b(kThreads);
 #define RTV_LAUNCH(DIM, MASK, QL, PL) \
   hipLaunchKernelGGL((attend_kernel<DIM, MASK, QL, PL>), g, b, 0, stream, args)
 #define RTV_DISPATCH_MASK(DIM, QL, PL) \

@@ -6,6 +6,27 @@
 
 namespace rtv {
 
+// Ring state of one layer in device memory (device-state mode): the calls
+// read it in their kernels and the advance kernel moves it, so that a
+// captured sequence of calls replays correctly step after step.
+struct DevRingState {
+  int64_t next_global_frame;
+  int32_t committed;
+  int32_t error;          // set (and kept) when a call finds the state unusable,
+                          // e.g. the chunk past the end of the RoPE table; the
+                          // call's kernels then write nothing
+};
+
+// Fixed shape of the ring, for the device-state mode.
+struct RingShape {
+  int32_t tokens_per_frame;
+  int32_t chunk_frames;
+  int32_t capacity_frames;
+  int32_t max_global_frames;
+  int32_t max_window_frames;  // attend only (0 = all valid)
+  int32_t head_dim;
+};
+
 struct AppendArgs {
   const uint16_t* k;      // [n][H][D] bf16, row stride ldk elements
   const uint16_t* v;
@@ -21,6 +42,12 @@ struct AppendArgs {
   int32_t n_heads;        // KV heads
   int32_t first_tile;     // write_slot / 64
   int32_t n_work;         // (#64-slot tiles touched) * n_heads
+  // device-state mode (dstate != nullptr): rope, write_slot, first_tile and
+  // n_work are derived in the kernel from *dstate; the grid covers the most
+  // tiles a chunk can touch
+  DevRingState* dstate;
+  const float* rope_table;  // position 0 of the RoPE table
+  RingShape shape;
 };
 
 struct AttendArgs {
@@ -58,7 +85,44 @@ struct AttendArgs {
   uint8_t* fac_u;         // [n_kv_heads][ring tiles][2][64] e4m3 rows of 2^-2 / rho
   int32_t n_kv_heads;
   int32_t ring_tiles;     // slots_padded / 64
+  // device-state mode (dstate != nullptr): rope, the segments and the
+  // schedule are derived in the kernels from *dstate; the grids cover the
+  // largest window
+  DevRingState* dstate;
+  const float* rope_table;
+  RingShape shape;
 };
+
+// Split schedule of an attention call over n_tiles window tiles, shared by
+// the host (host-state mode) and the kernels (device-state mode): whole
+// rounds of the device's concurrent workgroups run whole windows; the
+// remainder, which would leave most of the device idle in a last round, is
+// split along the keys into parts (at most max_parts) so that it fills one
+// short round.
+__host__ __device__ inline void attend_schedule(AttendArgs& a, int n_tiles, int max_parts) {
+  const int cap = a.capacity;
+  const int U = a.n_work;
+  int rem = cap > 0 ? U % cap : 0;
+  int S = rem > 0 ? cap / rem : 1;
+  if (S > n_tiles) S = n_tiles;
+  if ((int64_t)rem * S > max_parts) S = max_parts / (rem > 0 ? rem : 1);
+  if (S < 2 || !a.ws_o) { S = 1; rem = 0; }
+  a.n_full = U - rem;
+  a.parts_per_unit = S;
+  a.n_parts = rem * S;
+  a.full_per_xcd = (a.n_full + 7) / 8;
+  a.parts_per_xcd = (a.n_parts + 7) / 8;
+}
+
+// number of 64-slot tiles the window segments of a touch
+__host__ __device__ inline int attend_segment_tiles(int64_t lo, int64_t hi) {
+  return hi > lo ? (int)((hi - 1) / 64 - lo / 64 + 1) : 0;
+}
+__host__ __device__ inline int attend_window_tiles(const AttendArgs& a) {
+  // (constant indices only: the device copy of the arguments stays in registers)
+  return (a.n_segments > 0 ? attend_segment_tiles(a.seg_lo[0], a.seg_hi[0]) : 0) +
+         (a.n_segments > 1 ? attend_segment_tiles(a.seg_lo[1], a.seg_hi[1]) : 0);
+}
 
 // concurrent workgroups per device and workspace bound of the attention kernel
 int attend_max_parts();
@@ -77,6 +141,8 @@ int attend_queries_per_block();
 int quant_max_partials();
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, uint8_t* codes, float* scale,
                             uint32_t* partial, hipStream_t stream);
+// device-state mode: advance n layers' states by one chunk
+hipError_t launch_advance(DevRingState* s, int n, int chunk_frames, int capacity_frames, hipStream_t stream);
 hipError_t launch_gemm_fp8(const uint8_t* a, const float* sa, const uint8_t* bt, const float* sb,
                            uint16_t* c, int M, int N, int K, int64_t ldc, hipStream_t stream);
 

@@ -1,4 +1,5 @@
-// Ring arithmetic of the frame-granular KV cache (host only, header-only).
+// Ring arithmetic of the frame-granular KV cache (header-only; host and
+// device: the device-state mode derives the same windows in the kernels).
 //
 // The cache keeps the last C frames of a layer in a circular buffer and
 // advances by moving a head index instead of copying (page "Runway explains
@@ -18,6 +19,7 @@
 // C*T - 1.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace rtv {
@@ -32,7 +34,7 @@ struct RingWindow {
 
 enum RingStatus { kRingOk = 0, kRingBadArg = -1 };
 
-inline int ring_window(int64_t next_global_frame, int32_t committed, int32_t T, int32_t F,
+__host__ __device__ inline int ring_window(int64_t next_global_frame, int32_t committed, int32_t T, int32_t F,
                        int32_t C, int32_t max_window, RingWindow* w) {
   if (!w || T < 1 || F < 1 || C < F || C % F != 0) return kRingBadArg;
   if (committed < 0 || committed > C || next_global_frame < 0) return kRingBadArg;

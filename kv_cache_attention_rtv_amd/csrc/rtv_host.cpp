@@ -5,7 +5,12 @@
 // so the hot path never reads device memory back (a single host read-back per
 // step is reported to have raised the step time from 168.5 ms to 278 ms: page
 // "Runway explains how it serves a 57B video model in real time", fifth
-// paragraph).
+// paragraph).  For graph capture (the forward pass is captured in a CUDA
+// graph: page "Runway partage la construction de Runway Characters", fourth
+// paragraph) the state can instead live in the arena between
+// rtv_device_state_begin and rtv_device_state_end: the kernels then read it
+// and the advance is a kernel, so the enqueued work does not depend on host
+// values that a captured graph would freeze.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -38,7 +43,8 @@ struct LayerState {
 
 struct Plan {
   int64_t slots = 0, slots_padded = 0;
-  size_t rope_bytes = 0, ws_bytes = 0, codes_bytes = 0, scales_bytes = 0, layer_bytes = 0, total = 0;
+  size_t rope_bytes = 0, ws_bytes = 0, state_bytes = 0, codes_bytes = 0, scales_bytes = 0, layer_bytes = 0,
+         total = 0;
 };
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
@@ -79,13 +85,15 @@ rtv_status make_plan(const rtv_config* c, Plan* p) {
   p->rope_bytes = align_up((size_t)tmp);
   // attention workspace (partial results of split key ranges), shared by all layers
   p->ws_bytes = align_up(rtv::attend_workspace_bytes(c->head_dim, c->n_kv_heads, Sp));
+  // per-layer ring state for the device-state mode
+  p->state_bytes = align_up((size_t)c->n_layers * sizeof(rtv::DevRingState));
   if (!mul_ok((int64_t)c->n_kv_heads * c->head_dim, Sp, &tmp)) return RTV_ERR_INVALID_ARG;
   p->codes_bytes = align_up((size_t)tmp);
   p->scales_bytes = align_up((size_t)c->n_kv_heads * (size_t)Sp * 4);
   p->layer_bytes = 2 * p->codes_bytes + 2 * p->scales_bytes;
   int64_t layers_total;
   if (!mul_ok((int64_t)p->layer_bytes, c->n_layers, &layers_total)) return RTV_ERR_INVALID_ARG;
-  p->total = p->rope_bytes + p->ws_bytes + (size_t)layers_total;
+  p->total = p->rope_bytes + p->ws_bytes + p->state_bytes + (size_t)layers_total;
   return RTV_OK;
 }
 
@@ -120,6 +128,17 @@ void fill_rope(int32_t D, double base, int64_t pos0, int64_t npos, float* out) {
   for (auto& th : pool) th.join();
 }
 
+rtv::RingShape ring_shape(const rtv_config& cfg, int32_t max_window_frames) {
+  rtv::RingShape s;
+  s.tokens_per_frame = cfg.tokens_per_frame;
+  s.chunk_frames = cfg.chunk_frames;
+  s.capacity_frames = cfg.capacity_frames;
+  s.max_global_frames = cfg.max_global_frames;
+  s.max_window_frames = max_window_frames;
+  s.head_dim = cfg.head_dim;
+  return s;
+}
+
 }  // namespace
 
 struct rtv_cache {
@@ -128,6 +147,8 @@ struct rtv_cache {
   uint8_t* base = nullptr;
   float* rope = nullptr;
   float* ws = nullptr;          // attention workspace
+  rtv::DevRingState* dstate = nullptr;  // per-layer ring state in the arena
+  bool device_state = false;    // between rtv_device_state_begin and _end
   int capacity = 0;             // concurrent attention workgroups on the device
   std::vector<LayerState> layers;
 };
@@ -199,8 +220,9 @@ rtv_status rtv_cache_create(const rtv_config* cfg, void* dev_buf, size_t bytes, 
   c->base = static_cast<uint8_t*>(dev_buf);
   c->rope = reinterpret_cast<float*>(c->base);
   c->ws = reinterpret_cast<float*>(c->base + p.rope_bytes);
+  c->dstate = reinterpret_cast<rtv::DevRingState*>(c->base + p.rope_bytes + p.ws_bytes);
   c->layers.resize(cfg->n_layers);
-  uint8_t* cur = c->base + p.rope_bytes + p.ws_bytes;
+  uint8_t* cur = c->base + p.rope_bytes + p.ws_bytes + p.state_bytes;
   for (auto& L : c->layers) {
     L.kc = cur; cur += p.codes_bytes;
     L.vc = cur; cur += p.codes_bytes;
@@ -275,29 +297,47 @@ rtv_status rtv_append_rope_quant(rtv_cache* c, int32_t layer, const void* k_bf16
   if (k_tok_stride < row || v_tok_stride < row || k_tok_stride % 8 || v_tok_stride % 8)
     return RTV_ERR_INVALID_ARG;
   LayerState& L = c->layers[layer];
-  if (L.next_global_frame + cfg.chunk_frames > cfg.max_global_frames) return RTV_ERR_STATE;
-
-  rtv::RingWindow w;
-  if (rtv::ring_window(L.next_global_frame, L.committed, cfg.tokens_per_frame, cfg.chunk_frames,
-                       cfg.capacity_frames, 0, &w) != rtv::kRingOk)
-    return RTV_ERR_STATE;
   rtv::AppendArgs a;
+  a.dstate = nullptr;
+  a.rope_table = c->rope;
+  a.shape = ring_shape(cfg, 0);
+  rtv::RingWindow w;
+  if (c->device_state) {
+    // the kernel derives the slots and RoPE rows from the state in the arena;
+    // the grid covers the most 64-slot tiles a chunk can touch
+    a.dstate = c->dstate + layer;
+    w.write_slot = 0;
+    a.write_slot = 0;
+    a.first_tile = 0;
+    a.rope = c->rope;
+  } else {
+    if (L.next_global_frame + cfg.chunk_frames > cfg.max_global_frames) return RTV_ERR_STATE;
+    if (rtv::ring_window(L.next_global_frame, L.committed, cfg.tokens_per_frame, cfg.chunk_frames,
+                         cfg.capacity_frames, 0, &w) != rtv::kRingOk)
+      return RTV_ERR_STATE;
+  }
   a.k = static_cast<const uint16_t*>(k_bf16);
   a.v = static_cast<const uint16_t*>(v_bf16);
   a.ldk = k_tok_stride;
   a.ldv = v_tok_stride;
-  a.rope = c->rope + L.next_global_frame * cfg.tokens_per_frame * cfg.head_dim;
   a.kc = L.kc;
   a.vc = L.vc;
   a.ks = L.ks;
   a.vs = L.vs;
   a.slots_padded = c->plan.slots_padded;
-  a.write_slot = w.write_slot;
   a.n_tokens = n_tokens;
   a.n_heads = cfg.n_kv_heads;
-  a.first_tile = (int32_t)(w.write_slot / kTile);
-  const int64_t last_tile = (w.write_slot + n_tokens - 1) / kTile;
-  const int64_t n_work = (last_tile - a.first_tile + 1) * cfg.n_kv_heads;
+  int64_t n_work;
+  if (c->device_state) {
+    n_work = ((int64_t)n_tokens + kTile - 1) / kTile + 1;
+    n_work *= cfg.n_kv_heads;
+  } else {
+    a.rope = c->rope + L.next_global_frame * cfg.tokens_per_frame * cfg.head_dim;
+    a.write_slot = w.write_slot;
+    a.first_tile = (int32_t)(w.write_slot / kTile);
+    const int64_t last_tile = (w.write_slot + n_tokens - 1) / kTile;
+    n_work = (last_tile - a.first_tile + 1) * cfg.n_kv_heads;
+  }
   if (n_work > INT32_MAX / 2) return RTV_ERR_UNSUPPORTED;
   a.n_work = (int32_t)n_work;
   if (rtv::launch_append(a, cfg.head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -322,16 +362,24 @@ rtv_status rtv_attend(rtv_cache* c, int32_t layer, const void* q_bf16, int64_t q
   LayerState& L = c->layers[layer];
   if (!L.appended) return RTV_ERR_STATE;
   rtv::RingWindow w;
-  if (rtv::ring_window(L.next_global_frame, L.committed, cfg.tokens_per_frame, cfg.chunk_frames,
-                       cfg.capacity_frames, max_window_frames, &w) != rtv::kRingOk)
+  if (c->device_state) {
+    // the kernels derive the window, the RoPE rows and the schedule
+    w.n_segments = 0;
+    for (int i = 0; i < 2; ++i) w.seg_start[i] = w.seg_len[i] = 0;
+  } else if (rtv::ring_window(L.next_global_frame, L.committed, cfg.tokens_per_frame, cfg.chunk_frames,
+                              cfg.capacity_frames, max_window_frames, &w) != rtv::kRingOk) {
     return RTV_ERR_STATE;
+  }
   const int32_t n_tokens = cfg.chunk_frames * cfg.tokens_per_frame;
   rtv::AttendArgs a;
+  a.dstate = c->device_state ? c->dstate + layer : nullptr;
+  a.rope_table = c->rope;
+  a.shape = ring_shape(cfg, max_window_frames);
   a.q = static_cast<const uint16_t*>(q_bf16);
   a.out = static_cast<uint16_t*>(out_bf16);
   a.ldq = q_tok_stride;
   a.ldo = out_tok_stride;
-  a.rope = c->rope + L.next_global_frame * cfg.tokens_per_frame * cfg.head_dim;
+  a.rope = c->device_state ? c->rope : c->rope + L.next_global_frame * cfg.tokens_per_frame * cfg.head_dim;
   a.kc = L.kc;
   a.vc = L.vc;
   a.ks = L.ks;
@@ -357,12 +405,18 @@ rtv_status rtv_attend(rtv_cache* c, int32_t layer, const void* q_bf16, int64_t q
 }
 
 rtv_status rtv_advance(rtv_cache* c, int32_t layer, void* stream) {
-  (void)stream;
   if (!c || layer < -1 || layer >= c->cfg.n_layers) return RTV_ERR_INVALID_ARG;
   const int lo = layer < 0 ? 0 : layer;
   const int hi = layer < 0 ? c->cfg.n_layers : layer + 1;
   for (int l = lo; l < hi; ++l)
     if (!c->layers[l].appended) return RTV_ERR_STATE;
+  if (c->device_state) {
+    if (rtv::launch_advance(c->dstate + lo, hi - lo, c->cfg.chunk_frames, c->cfg.capacity_frames,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
+      return RTV_ERR_HIP;
+    for (int l = lo; l < hi; ++l) c->layers[l].appended = 0;
+    return RTV_OK;
+  }
   for (int l = lo; l < hi; ++l) {
     LayerState& L = c->layers[l];
     L.next_global_frame += c->cfg.chunk_frames;
@@ -370,6 +424,43 @@ rtv_status rtv_advance(rtv_cache* c, int32_t layer, void* stream) {
     L.appended = 0;
   }
   return RTV_OK;
+}
+
+rtv_status rtv_device_state_begin(rtv_cache* c, void* stream) {
+  if (!c) return RTV_ERR_INVALID_ARG;
+  if (c->device_state) return RTV_ERR_STATE;
+  std::vector<rtv::DevRingState> st(c->layers.size());
+  for (size_t l = 0; l < st.size(); ++l) {
+    st[l].next_global_frame = c->layers[l].next_global_frame;
+    st[l].committed = c->layers[l].committed;
+    st[l].error = 0;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(c->dstate, st.data(), st.size() * sizeof(rtv::DevRingState),
+                                hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return RTV_ERR_HIP;
+  c->device_state = true;
+  return RTV_OK;
+}
+
+rtv_status rtv_device_state_end(rtv_cache* c, void* stream) {
+  if (!c) return RTV_ERR_INVALID_ARG;
+  if (!c->device_state) return RTV_ERR_STATE;
+  std::vector<rtv::DevRingState> st(c->layers.size());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(st.data(), c->dstate, st.size() * sizeof(rtv::DevRingState),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return RTV_ERR_HIP;
+  bool error = false;
+  for (size_t l = 0; l < st.size(); ++l) {
+    c->layers[l].next_global_frame = st[l].next_global_frame;
+    c->layers[l].committed = st[l].committed;
+    error = error || st[l].error != 0;
+  }
+  c->device_state = false;
+  return error ? RTV_ERR_STATE : RTV_OK;
 }
 
 rtv_status rtv_encode_e4m3(const float* x_dev, uint8_t* codes_dev, int64_t n, void* stream) {
