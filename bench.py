@@ -13,6 +13,13 @@ ring is filled before the warm-up steps, so all timed steps run in the steady
 state (full 16-frame window; the four growth steps of a fresh cache are
 cheaper and not part of the figure).
 
+By default the timed steps are replays of one HIP graph holding the whole step
+(240 appends, 240 attends, the advance), captured once with the ring state in
+device memory, as the pages capture the forward pass in a CUDA graph (page
+"Runway partage la construction de Runway Characters", fourth paragraph).  The
+per-call figures (roofline) come from eagerly launched steps with HIP events
+around every call; `--eager` times eager steps for the headline figure too.
+
 Prints ONE JSON line (see --help).  The oracle leg (cpu_baseline) times the CPU
 oracle on a bounded sample of the same workload and scales it to one step.
 """
@@ -39,6 +46,10 @@ def parse():
     p.add_argument("--layers", type=int, default=60)
     p.add_argument("--calls", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager", action="store_true",
+                   help="time eagerly launched steps (default: replays of one captured HIP graph per step)")
+    p.add_argument("--call-steps", type=int, default=2,
+                   help="eager steps with HIP events around every call, for the per-call figures")
     p.add_argument("--cpu-heads", type=int, default=8,
                    help="query heads (all chunk rows) the oracle attends in the cpu_baseline sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -228,7 +239,11 @@ def main():
     wl = dataclasses.replace(get_workload("step"), n_layers=args.layers, calls_per_layer=args.calls)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    total_steps = wl.capacity_frames // wl.chunk_frames + args.warmup + args.steps
+    # steps the run makes: ring fill, warm-up, eager steps with per-call
+    # events, and (graph mode) one eager device-state step, warm-up replays
+    # and the timed replays; the RoPE table covers them all
+    total_steps = wl.capacity_frames // wl.chunk_frames + args.warmup + (
+        args.steps if args.eager else args.call_steps + 1 + args.warmup + args.steps)
     cfg = rtv.RtvConfig(wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
                         wl.tokens_per_frame, wl.chunk_frames, wl.capacity_frames,
                         (total_steps + 1) * wl.chunk_frames, wl.rope_base)
@@ -269,22 +284,56 @@ def main():
     for s in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
+
+    def timed(k, body):
+        """k steps of body() between HIP events on the stream; (GPU ms, wall s)."""
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(k):
+            body()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end), time.perf_counter() - wall0
+
+    # eager steps with an event pair around every call: the per-call figures
     ev = ([], [], [])
-    step_start = torch.cuda.Event(enable_timing=True)
-    step_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    step_start.record(stream)
-    for s in range(args.steps):
+    n_call_steps = args.steps if args.eager else args.call_steps
+
+    def eager_step():
         windows.append(cache.window(0).window_frames)
         run_step(ev)
-    step_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    gpu_ms = step_start.elapsed_time(step_end)
+    eager_ms, eager_wall = timed(n_call_steps, eager_step)
+    mode = "eager launches"
+    if args.eager:
+        gpu_ms, wall = eager_ms, eager_wall
+    else:
+        # one step captured in a HIP graph with the ring state in device
+        # memory; warm-up replays, then the timed replays
+        cache.device_state_begin(stream=stream)
+        run_step()                            # eager step in the device-state mode
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        torch.cuda.synchronize()
+        main_stream = stream
+        stream = side
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                run_step()
+        stream = main_stream
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        gpu_ms, wall = timed(args.steps, graph.replay)
+        cache.device_state_end(stream=stream)
+        windows.append(cache.window(0).window_frames)
+        mode = "one HIP graph per step (device-resident ring state), replayed"
     ms_per_step = gpu_ms / args.steps
 
-    per_call_windows = [w for w in windows for _ in range(wl.calls_per_layer * wl.n_layers)]
+    per_call_windows = [w for w in windows[:n_call_steps] for _ in range(wl.calls_per_layer * wl.n_layers)]
     app_ms = [a.elapsed_time(b) for a, b in zip(ev[0], ev[1])]
     att_ms = [a.elapsed_time(b) for a, b in zip(ev[1], ev[2])]
     app_bytes = algorithmic(wl, 0)[0]
@@ -326,8 +375,9 @@ def main():
                          f"{H} KV heads x {D}, {Hq} query heads, {wl.tokens_per_frame} tokens/frame, "
                          f"{n}-token chunks, {wl.capacity_frames}-frame ring ({wl.capacity_tokens} slots)"),
             "global_batch": 1, "seq_len": n, "window_frames_timed": sorted(set(windows)),
-            "parallelism": "none (one GPU's head share)",
+            "parallelism": "none (one GPU's head share)", "launch": mode,
         },
+        "eager_ms_per_step": round(eager_ms / n_call_steps, 3),
         "roofline": {
             "bound": "mfma",
             "kernel": ("rtv_attend = factors_kernel + attend_kernel<128, false, false, false> + "

@@ -3,7 +3,7 @@ FP8 GEMM with float32-or-better accumulation.
 
 The pages name a fused FP8 matmul in the serving step (page "Runway explains how
 it serves a 57B video model in real time", fourth paragraph) and matmul tuning
-(page "Runway partage la construction de Runway Characters", third paragraph)
+(page "Runway partage la construction de Runway Characters", fourth paragraph)
 without a formula.  Reading taken:
 
     s_x = f32(amax(X) / 448),  Xq = e4m3.encode(f32(X / s_x))     (per tensor)
