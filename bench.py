@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true",
                    help="time eagerly launched steps (default: replays of one captured HIP graph per step)")
+    p.add_argument("--workload", choices=["step", "projection"], default="step",
+                   help="projection: time the projection workload's chunk (per-tensor e4m3 of X, the FP8 "
+                        "QKV GEMM and the append) unfused and fused, one JSON line")
     p.add_argument("--call-steps", type=int, default=2,
                    help="eager steps with HIP events around every call, for the per-call figures")
     p.add_argument("--cpu-heads", type=int, default=8,
@@ -219,8 +222,98 @@ def cpu_baseline(wl, heads: int):
     }
 
 
+def projection(args):
+    """The projection workload's chunk: X [11968 x 6144] bf16 to e4m3 (per
+    tensor), then either the FP8 GEMM to bf16 QKV [11968 x 4608] followed by
+    the append of its K/V columns (unfused), or the GEMM whose epilogue writes
+    K/V into the ring (rtv_qkv_gemm_append).  Inputs N(0,1) (W N(0, 1/6144)),
+    drawn on the device."""
+    import torch
+
+    import kv_cache_attention_rtv_amd as rtv
+    from workloads import get_workload
+    from workloads.generate import device_normal_bf16
+
+    wl = get_workload("proj")
+    dev = torch.device("cuda:0")
+    H, D = wl.n_kv_heads, wl.head_dim
+    n, hid, N = wl.chunk_tokens, wl.hidden, wl.proj_width
+    q_cols = N - 2 * H * D
+    reps = args.steps
+    total = 2 * (args.warmup + reps) + 2
+    cfg = rtv.RtvConfig(1, wl.n_q_heads, H, D, wl.tokens_per_frame, wl.chunk_frames, wl.capacity_frames,
+                        total * wl.chunk_frames, wl.rope_base)
+    cache = rtv.RtvCache(cfg, device=dev)
+    x = device_normal_bf16((n, hid), (4, 0, 0), dev)
+    wt = (device_normal_bf16((N, hid), (4, 0, 1), dev).float() * (1.0 / hid ** 0.5)).to(torch.bfloat16)
+    xc, sx = rtv.quant_fp8_per_tensor(x)
+    wc, sw = rtv.quant_fp8_per_tensor(wt)
+    qkv = torch.empty((n, N), dtype=torch.bfloat16, device=dev)
+    q_out = torch.empty((n, q_cols), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(rtv.abi.rtv_quant_workspace_bytes(x.numel()), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def quant():
+        rtv.quant_fp8_per_tensor(x, xc, sx, ws)
+
+    def gemm():
+        rtv.gemm_fp8(xc, sx, wc, sw, qkv)
+
+    def append():
+        k = qkv[:, q_cols:q_cols + H * D].unflatten(1, (H, D))
+        v = qkv[:, q_cols + H * D:].unflatten(1, (H, D))
+        cache.append(0, k, v, stream=stream)
+        cache.advance(0, stream=stream)
+
+    def fused():
+        rtv.qkv_gemm_append(cache, 0, xc, sx, wc, sw, q_cols, q_out)
+        cache.advance(0, stream=stream)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    gemm()
+    torch.cuda.synchronize()
+    t_quant = timed(quant)
+    t_gemm = timed(gemm)
+    t_append = timed(append)
+    t_fused = timed(fused)
+    flops = 2.0 * n * hid * N
+    unfused = t_quant + t_gemm + t_append
+    result = {
+        "metric": "ms per projection chunk (per-tensor e4m3 of X, FP8 QKV GEMM, K/V into the ring)",
+        "value": round(t_quant + t_fused, 4), "unit": "ms", "higher_is_better": False,
+        "steps": reps, "warmup": args.warmup, "dtype": "fp8-e4m3 (f32 accumulate)", "data": "synthetic",
+        "config": {"workload": f"X [{n} x {hid}] bf16, Wt [{N} x {hid}] (Q {q_cols} + K {H * D} + V {H * D} "
+                               f"columns), {H} KV heads x {D}, {wl.capacity_frames}-frame ring"},
+        "quant_ms": round(t_quant, 4), "gemm_ms": round(t_gemm, 4), "append_ms": round(t_append, 4),
+        "unfused_ms": round(unfused, 4), "fused_gemm_append_ms": round(t_fused, 4),
+        "fused_ms": round(t_quant + t_fused, 4),
+        "gemm_tflops": round(flops / (t_gemm * 1e-3) / 1e12, 1),
+        "fused_gemm_tflops": round(flops / (t_fused * 1e-3) / 1e12, 1),
+        "gemm_frac_fp8_peak": round(flops / (t_gemm * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "fused_frac_fp8_peak": round(flops / (t_fused * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload == "projection":
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        projection(args)
+        return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_bytes, args.traffic_json)
         return

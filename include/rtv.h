@@ -248,6 +248,32 @@ rtv_status rtv_gemm_fp8(const uint8_t* a, const float* sa_dev, const uint8_t* bt
                         const float* sb_dev, void* c_bf16, int32_t M, int32_t N,
                         int32_t K, int64_t ldc, void* stream);
 
+/* The projection GEMM fused with the cache upkeep (the fused FP8 matmul of
+ * [aidose.in, fourth paragraph], whose K/V enter the cache with RoPE and FP8
+ * applied at write time, same paragraph): for the n_tokens = chunk_frames *
+ * tokens_per_frame tokens of the current chunk of `layer`,
+ *   QKV[m][n] = (*sx_dev) * (*sw_dev) * sum_k dec(x_codes[m][k]) * dec(wt_codes[n][k])
+ * with f32 accumulation, columns ordered [q_cols Q columns | n_kv_heads K heads
+ * | n_kv_heads V heads] (head_dim columns per head).  Q columns are written
+ * to q_bf16 ([n_tokens][q_tok_stride] bf16) exactly as rtv_gemm_fp8 writes
+ * them.  K and V never go through bf16: from the f32 values the epilogue
+ * applies RoPE to K at the chunk's positions and quantizes each (token, head)
+ * row with the append's rule (scale = RN(amax/448), code = e4m3(RN(x/scale)))
+ * into the chunk's ring slots, then counts as the layer's append.  It equals
+ * rtv_gemm_fp8 followed by rtv_append_rope_quant except for the bf16 rounding
+ * of K and V in between (codes may differ by one step).
+ *   x_codes: [n_tokens][k_dim] e4m3; wt_codes: [q_cols + 2*n_kv_heads*head_dim][k_dim]
+ *   e4m3 (the weight transposed); k_dim a multiple of 64; q_cols a multiple of
+ *   head_dim (0 = no Q columns, q_bf16 may then be NULL).
+ * Errors: INVALID_ARG (shapes, pointers, alignment), STATE (RoPE table
+ * exhausted), UNSUPPORTED (a chunk that is not a multiple of 64 tokens, or
+ * the device-state mode). */
+rtv_status rtv_qkv_gemm_append(rtv_cache* cache, int32_t layer,
+                               const uint8_t* x_codes, const float* sx_dev,
+                               const uint8_t* wt_codes, const float* sw_dev,
+                               int32_t n_tokens, int32_t k_dim, int32_t q_cols,
+                               void* q_bf16, int64_t q_tok_stride, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,6 +8,6 @@ been built: there is no CPU fallback.
 from . import abi
 from .abi import RtvError
 from .cache import RtvCache, RtvConfig
-from .projection import gemm_fp8, quant_fp8_per_tensor
+from .projection import gemm_fp8, qkv_gemm_append, quant_fp8_per_tensor
 
-__all__ = ["abi", "RtvError", "RtvCache", "RtvConfig", "gemm_fp8", "quant_fp8_per_tensor"]
+__all__ = ["abi", "RtvError", "RtvCache", "RtvConfig", "gemm_fp8", "qkv_gemm_append", "quant_fp8_per_tensor"]

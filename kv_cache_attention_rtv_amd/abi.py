@@ -94,6 +94,7 @@ def _load():
         "rtv_quant_workspace_bytes": (SZ, [I64]),
         "rtv_quant_fp8_per_tensor": (I32, [P, I64, P, P, P, P]),
         "rtv_gemm_fp8": (I32, [P, P, P, P, P, I32, I32, I32, I64, P]),
+        "rtv_qkv_gemm_append": (I32, [P, I32, P, P, P, P, I32, I32, I32, P, I64, P]),
     }
     missing = []
     for name, (res, args) in sigs.items():
@@ -113,7 +114,7 @@ EXPORTED = (
     "rtv_cache_bytes", "rtv_cache_create", "rtv_destroy", "rtv_append_rope_quant",
     "rtv_attend", "rtv_advance", "rtv_device_state_begin", "rtv_device_state_end", "rtv_cache_layout", "rtv_cache_window", "rtv_ring_window",
     "rtv_rope_fill_host", "rtv_encode_e4m3", "rtv_status_string",
-    "rtv_quant_workspace_bytes", "rtv_quant_fp8_per_tensor", "rtv_gemm_fp8",
+    "rtv_quant_workspace_bytes", "rtv_quant_fp8_per_tensor", "rtv_gemm_fp8", "rtv_qkv_gemm_append",
 )
 
 
@@ -210,3 +211,9 @@ def rtv_quant_fp8_per_tensor(x_ptr, n, codes_ptr, scale_ptr, ws_ptr, stream):
 
 def rtv_gemm_fp8(a_ptr, sa_ptr, bt_ptr, sb_ptr, c_ptr, M, N, K, ldc, stream):
     check(lib.rtv_gemm_fp8(a_ptr, sa_ptr, bt_ptr, sb_ptr, c_ptr, M, N, K, ldc, stream), "rtv_gemm_fp8")
+
+
+def rtv_qkv_gemm_append(handle, layer, x_ptr, sx_ptr, wt_ptr, sw_ptr, n_tokens, k_dim, q_cols,
+                        q_ptr, q_tok_stride, stream):
+    check(lib.rtv_qkv_gemm_append(handle, layer, x_ptr, sx_ptr, wt_ptr, sw_ptr, n_tokens, k_dim, q_cols,
+                                  q_ptr, q_tok_stride, stream), "rtv_qkv_gemm_append")

@@ -43,12 +43,6 @@ __device__ __forceinline__ float dpp_max8(float x) {
   return fmaxf(x, y);
 }
 
-// position of key `k` (0..63) inside a transposed V tile row
-__device__ __forceinline__ int vt_pos_of_key(int k) {
-  const int h = (k >> 2) & 1;
-  const int b = ((k >> 5) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
-  return h * 32 + b;
-}
 // first key of the 4 consecutive positions 4*p4 .. 4*p4+3
 __device__ __forceinline__ int vt_key_of_pos4(int p4) {
   const int h = p4 >> 3;

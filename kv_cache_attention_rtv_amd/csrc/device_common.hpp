@@ -8,6 +8,14 @@ namespace rtv {
 
 constexpr int kWave = 64;
 constexpr int kTileKeys = 64;          // slots per V-transposed tile / attention key tile
+
+// position of key `k` (0..63) inside a transposed V tile row (the byte order
+// of the attention's matrix-core operand)
+__device__ __forceinline__ int vt_pos_of_key(int k) {
+  const int h = (k >> 2) & 1;
+  const int b = ((k >> 5) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+  return h * 32 + b;
+}
 constexpr float kFp8Max = 448.0f;
 
 // ---- bf16 ---------------------------------------------------------------

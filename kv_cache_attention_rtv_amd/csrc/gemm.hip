@@ -18,6 +18,20 @@
 // Tiles are numbered XCD-aware (each XCD walks a contiguous range) and grouped
 // four M-rows at a time so the workgroups resident on one XCD share operands
 // in its L2.
+//
+// Fused QKV epilogue (gemm_fp8_kernel<D>, D = head_dim): the output columns
+// are [Q heads | K heads | V heads] of one chunk's tokens.  Q columns are
+// written as bf16 like the plain GEMM; K and V heads never reach HBM in bf16:
+// from the f32 result (times s_a s_b) the epilogue applies RoPE to K at the
+// chunk's positions and quantizes each (token, head) row to e4m3 with the
+// cache's row rule, straight into the ring slots of the current chunk (the
+// fused FP8 matmul of page "Runway explains how it serves a 57B video model in
+// real time", fourth paragraph, with the write-time RoPE and FP8 of the same
+// paragraph).  The accumulator tile goes through LDS (f32, 128 tokens at a
+// time); then each wave takes one 64-token ring tile of one head, one lane per
+// token, so a row's RoPE pairs and amax stay in one lane (plus one exchange
+// between the two waves of a 128-wide head), K rows are written as 32-byte
+// runs and the transposed V tile as 64-byte rows.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -128,6 +142,17 @@ struct GemmArgs {
   int32_t M, N, K;
   int32_t n_mt, n_nt, n_tiles;
   int32_t vec_store;   // 8-byte stores allowed (c 8-aligned, ldc % 4 == 0)
+  // fused QKV epilogue: columns [0, q_cols) are Q (bf16 into c), then
+  // n_kv_heads K heads and n_kv_heads V heads of D columns into the ring
+  int32_t q_cols;
+  int32_t n_kv_heads;
+  const float* rope;   // (cos, sin) pairs of the chunk's first position: [M][D/2][2]
+  uint8_t* kc;         // layer ring, as for the append
+  uint8_t* vc;
+  float* ks;
+  float* vs;
+  int64_t slots_padded;
+  int64_t write_slot;  // first slot of the chunk, a multiple of 64
 };
 
 // global -> register loads of one stage: chunk c of 16 bytes, rows [0, 256)
@@ -173,6 +198,133 @@ __device__ __forceinline__ v8i frag(const uint8_t* st, int row0, int ks, int lan
   return v;
 }
 
+constexpr int kEpiRow = kBN * 4 + 16;          // bytes per token row of the f32 tile in LDS
+constexpr int kEpiAmax = 128 * kEpiRow;         // per-row amax exchange after the tile
+
+// Fused epilogue of one 256 x 256 tile (see the file comment).  acc[i][j]
+// holds D[n][m] for m = m0+wm+32i + lane%32 and n = n0+wn+32j + 8(r/4) +
+// 4(lane/32) + r%4; tokens m >= M are skipped.
+template <int D, typename Acc>
+__device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc, float s, uint8_t* smem,
+                                               int m0, int n0, int wm, int wn, int wave, int lane) {
+  constexpr int HALF = D / 2;
+  constexpr int PARTS = D / 64;                  // waves per head (32 RoPE pairs each)
+  const int hh = lane >> 5;
+  float* amax_x = reinterpret_cast<float*>(smem + kEpiAmax);
+  const int kv_cols = g.n_kv_heads * D;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();                             // LDS free: operands or the previous half consumed
+    // (1) the wave's tokens m0 + wm + 64 half + [0, 64) -> rows (wm / 128) * 64 + [0, 64)
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int row = (wm / 128) * 64 + ii * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int grp4 = 0; grp4 < 4; ++grp4) {
+          const int n = wn + 32 * j + 8 * grp4 + 4 * hh;
+          const auto& a4 = acc[2 * half + ii][j];
+          *reinterpret_cast<float4*>(smem + row * kEpiRow + n * 4) =
+              make_float4(a4[4 * grp4] * s, a4[4 * grp4 + 1] * s, a4[4 * grp4 + 2] * s, a4[4 * grp4 + 3] * s);
+        }
+    }
+    __syncthreads();
+    // (2) wave -> (ring tile t, head of the tile, part); lane -> token
+    const int t = wave >> 2;
+    const int hp = wave & 3;
+    const int head_local = hp / PARTS;
+    const int part = hp % PARTS;
+    const int m = m0 + 128 * t + 64 * half + lane;
+    const bool valid = m < g.M;
+    const int col = n0 + head_local * D;         // first column of the head (uniform)
+    const float* erow = reinterpret_cast<const float*>(smem + (64 * t + lane) * kEpiRow) + head_local * D;
+    float x0[32], x1[32];
+#pragma unroll
+    for (int q = 0; q < 32; q += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(erow + 32 * part + q);
+      const float4 b = *reinterpret_cast<const float4*>(erow + HALF + 32 * part + q);
+      x0[q] = a.x; x0[q + 1] = a.y; x0[q + 2] = a.z; x0[q + 3] = a.w;
+      x1[q] = b.x; x1[q + 1] = b.y; x1[q + 2] = b.z; x1[q + 3] = b.w;
+    }
+    const bool is_q = col < g.q_cols;
+    const bool is_k = !is_q && col < g.q_cols + kv_cols;
+    const bool in_range = col < g.N;
+    if (is_k) {
+      // RoPE at position (chunk start) + m, rounded as in the append
+      const float* cs = g.rope + (int64_t)(valid ? m : 0) * D + 64 * part;
+#pragma unroll
+      for (int q = 0; q < 32; q += 2) {
+        const float4 c = *reinterpret_cast<const float4*>(cs + 2 * q);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float co = e ? c.z : c.x;
+          const float si = e ? c.w : c.y;
+          const float a0 = x0[q + e] * co;
+          const float b0 = x1[q + e] * si;
+          const float a1 = x1[q + e] * co;
+          const float b1 = x0[q + e] * si;
+          x0[q + e] = a0 - b0;
+          x1[q + e] = a1 + b1;
+        }
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fmaxf(fabsf(x0[q]), fabsf(x1[q])));
+    if constexpr (PARTS > 1) {
+      amax_x[wave * 64 + lane] = amax;
+      __syncthreads();
+      amax = fmaxf(amax, amax_x[(wave ^ 1) * 64 + lane]);
+    }
+    if (!valid || !in_range) continue;
+    if (is_q) {
+      uint16_t* dst = g.c + (int64_t)m * g.ldc + col + 32 * part;
+#pragma unroll
+      for (int q = 0; q < 32; q += 8) {
+        uint4 w0, w1;
+        w0.x = pack_bf16x2(x0[q], x0[q + 1]); w0.y = pack_bf16x2(x0[q + 2], x0[q + 3]);
+        w0.z = pack_bf16x2(x0[q + 4], x0[q + 5]); w0.w = pack_bf16x2(x0[q + 6], x0[q + 7]);
+        w1.x = pack_bf16x2(x1[q], x1[q + 1]); w1.y = pack_bf16x2(x1[q + 2], x1[q + 3]);
+        w1.z = pack_bf16x2(x1[q + 4], x1[q + 5]); w1.w = pack_bf16x2(x1[q + 6], x1[q + 7]);
+        *reinterpret_cast<uint4*>(dst + q) = w0;
+        *reinterpret_cast<uint4*>(dst + HALF + q) = w1;
+      }
+      continue;
+    }
+    const RowQuant rq = row_quant(amax);
+    uint32_t c0[8], c1[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      c0[q] = quant4(x0[4 * q], x0[4 * q + 1], x0[4 * q + 2], x0[4 * q + 3], rq);
+      c1[q] = quant4(x1[4 * q], x1[4 * q + 1], x1[4 * q + 2], x1[4 * q + 3], rq);
+    }
+    const int64_t slot = g.write_slot + m;
+    if (is_k) {
+      const int h = (col - g.q_cols) / D;
+      uint8_t* dst = g.kc + ((int64_t)h * g.slots_padded + slot) * D + 32 * part;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(c0[0], c0[1], c0[2], c0[3]);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(c0[4], c0[5], c0[6], c0[7]);
+      *reinterpret_cast<uint4*>(dst + HALF) = make_uint4(c1[0], c1[1], c1[2], c1[3]);
+      *reinterpret_cast<uint4*>(dst + HALF + 16) = make_uint4(c1[4], c1[5], c1[6], c1[7]);
+      if (part == 0) g.ks[(int64_t)h * g.slots_padded + slot] = rq.s;
+    } else {
+      // transposed V tile: byte vt_pos(slot % 64) of row d; the wave's 64
+      // lanes fill one 64-byte row per d
+      const int h = (col - g.q_cols - kv_cols) / D;
+      uint8_t* vt = g.vc + (((int64_t)h * (g.slots_padded / kTileKeys) + slot / kTileKeys) * D) * kTileKeys +
+                    vt_pos_of_key((int)(slot % kTileKeys));
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        vt[(int64_t)(32 * part + q) * kTileKeys] = (uint8_t)(c0[q >> 2] >> (8 * (q & 3)));
+        vt[(int64_t)(HALF + 32 * part + q) * kTileKeys] = (uint8_t)(c1[q >> 2] >> (8 * (q & 3)));
+      }
+      if (part == 0) g.vs[(int64_t)h * g.slots_padded + slot] = rq.s;
+    }
+  }
+}
+
+template <int FUSED_D>
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int logical = xcd_remap(blockIdx.x, g.n_tiles);
@@ -231,6 +383,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
   // epilogue: acc[i][j] holds D[n][m] for m = m0+wm+32i + lane%32 and
   // n = n0+wn+32j + 8(r/4) + 4(lane/32) + r%4
   const float s = (*g.sa) * (*g.sb);
+  if constexpr (FUSED_D > 0) {
+    fused_epilogue<FUSED_D>(g, acc, s, smem, m0, n0, wm, wn, wave, lane);
+    return;
+  }
   const int hh = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -274,21 +430,44 @@ hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, uint8_t* codes, float*
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_fp8(const uint8_t* a, const float* sa, const uint8_t* bt, const float* sb,
-                           uint16_t* c, int M, int N, int K, int64_t ldc, hipStream_t stream) {
-  const hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
-  if (e != hipSuccess) return e;
-  GemmArgs g;
+static GemmArgs gemm_args(const uint8_t* a, const float* sa, const uint8_t* bt, const float* sb, uint16_t* c,
+                          int M, int N, int K, int64_t ldc) {
+  GemmArgs g{};
   g.a = a; g.bt = bt; g.sa = sa; g.sb = sb; g.c = c; g.ldc = ldc;
   g.M = M; g.N = N; g.K = K;
   g.n_mt = (M + kBM - 1) / kBM;
   g.n_nt = (N + kBN - 1) / kBN;
   g.n_tiles = g.n_mt * g.n_nt;
   g.vec_store = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
+  return g;
+}
+
+template <int FUSED_D>
+static hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
+  const hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<FUSED_D>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
+  if (e != hipSuccess) return e;
   const int grid = (g.n_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL(gemm_fp8_kernel, dim3(grid), dim3(kGemmThreads), 2 * kStageBytes, stream, g);
+  hipLaunchKernelGGL(gemm_fp8_kernel<FUSED_D>, dim3(grid), dim3(kGemmThreads), 2 * kStageBytes, stream, g);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const uint8_t* a, const float* sa, const uint8_t* bt, const float* sb,
+                           uint16_t* c, int M, int N, int K, int64_t ldc, hipStream_t stream) {
+  return launch_gemm<0>(gemm_args(a, sa, bt, sb, c, M, N, K, ldc), stream);
+}
+
+hipError_t launch_qkv_gemm_append(const QkvAppendArgs& q, hipStream_t stream) {
+  static_assert(2 * kStageBytes >= kEpiAmax + kGemmWaves * 64 * 4, "fused epilogue fits the GEMM's LDS");
+  const int N = q.q_cols + 2 * q.n_kv_heads * q.head_dim;
+  GemmArgs g = gemm_args(q.x, q.sx, q.wt, q.sw, q.q_out, q.M, N, q.K, q.ldq);
+  g.q_cols = q.q_cols;
+  g.n_kv_heads = q.n_kv_heads;
+  g.rope = q.rope;
+  g.kc = q.kc; g.vc = q.vc; g.ks = q.ks; g.vs = q.vs;
+  g.slots_padded = q.slots_padded;
+  g.write_slot = q.write_slot;
+  return q.head_dim == 128 ? launch_gemm<128>(g, stream) : launch_gemm<64>(g, stream);
 }
 
 }  // namespace rtv

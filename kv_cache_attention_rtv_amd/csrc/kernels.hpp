@@ -141,6 +141,25 @@ int attend_queries_per_block();
 int quant_max_partials();
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, uint8_t* codes, float* scale,
                             uint32_t* partial, hipStream_t stream);
+// FP8 QKV GEMM whose epilogue writes Q as bf16 and K, V (RoPE on K, e4m3 per
+// (token, head)) straight into the ring slots of the chunk
+struct QkvAppendArgs {
+  const uint8_t* x;       // [M][K] e4m3
+  const float* sx;
+  const uint8_t* wt;      // [N][K] e4m3, N = q_cols + 2 * n_kv_heads * head_dim
+  const float* sw;
+  uint16_t* q_out;        // [M][ldq] bf16 (columns [0, q_cols))
+  int64_t ldq;
+  int32_t M, K, q_cols, n_kv_heads, head_dim;
+  const float* rope;      // (cos, sin) pairs of the chunk's first position
+  uint8_t* kc;
+  uint8_t* vc;
+  float* ks;
+  float* vs;
+  int64_t slots_padded;
+  int64_t write_slot;     // multiple of 64
+};
+hipError_t launch_qkv_gemm_append(const QkvAppendArgs& q, hipStream_t stream);
 // device-state mode: advance n layers' states by one chunk
 hipError_t launch_advance(DevRingState* s, int n, int chunk_frames, int capacity_frames, hipStream_t stream);
 hipError_t launch_gemm_fp8(const uint8_t* a, const float* sa, const uint8_t* bt, const float* sb,

@@ -426,6 +426,45 @@ rtv_status rtv_advance(rtv_cache* c, int32_t layer, void* stream) {
   return RTV_OK;
 }
 
+rtv_status rtv_qkv_gemm_append(rtv_cache* c, int32_t layer, const uint8_t* x_codes, const float* sx_dev,
+                               const uint8_t* wt_codes, const float* sw_dev, int32_t n_tokens, int32_t k_dim,
+                               int32_t q_cols, void* q_bf16, int64_t q_tok_stride, void* stream) {
+  if (!c || layer < 0 || layer >= c->cfg.n_layers) return RTV_ERR_INVALID_ARG;
+  const rtv_config& cfg = c->cfg;
+  const int64_t chunk = (int64_t)cfg.chunk_frames * cfg.tokens_per_frame;
+  if (n_tokens != chunk || k_dim <= 0 || k_dim % 64 != 0) return RTV_ERR_INVALID_ARG;
+  if (q_cols < 0 || q_cols % cfg.head_dim != 0) return RTV_ERR_INVALID_ARG;
+  if (!x_codes || !wt_codes || !sx_dev || !sw_dev || (q_cols > 0 && !q_bf16)) return RTV_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(x_codes) | reinterpret_cast<uintptr_t>(wt_codes) |
+       reinterpret_cast<uintptr_t>(q_bf16)) % 16 ||
+      (reinterpret_cast<uintptr_t>(sx_dev) | reinterpret_cast<uintptr_t>(sw_dev)) % 4)
+    return RTV_ERR_INVALID_ARG;
+  if (q_cols > 0 && (q_tok_stride < q_cols || q_tok_stride % 8 != 0)) return RTV_ERR_INVALID_ARG;
+  const int64_t n_cols = (int64_t)q_cols + 2 * (int64_t)cfg.n_kv_heads * cfg.head_dim;
+  if (n_cols > INT32_MAX) return RTV_ERR_INVALID_ARG;
+  // the epilogue writes whole 64-slot tiles; the host-state ring gives the slots
+  if (chunk % kTile != 0 || c->device_state) return RTV_ERR_UNSUPPORTED;
+  LayerState& L = c->layers[layer];
+  if (L.next_global_frame + cfg.chunk_frames > cfg.max_global_frames) return RTV_ERR_STATE;
+  rtv::RingWindow w;
+  if (rtv::ring_window(L.next_global_frame, L.committed, cfg.tokens_per_frame, cfg.chunk_frames,
+                       cfg.capacity_frames, 0, &w) != rtv::kRingOk)
+    return RTV_ERR_STATE;
+  rtv::QkvAppendArgs q;
+  q.x = x_codes; q.sx = sx_dev; q.wt = wt_codes; q.sw = sw_dev;
+  q.q_out = static_cast<uint16_t*>(q_bf16);
+  q.ldq = q_cols > 0 ? q_tok_stride : 0;
+  q.M = n_tokens; q.K = k_dim; q.q_cols = q_cols;
+  q.n_kv_heads = cfg.n_kv_heads; q.head_dim = cfg.head_dim;
+  q.rope = c->rope + L.next_global_frame * cfg.tokens_per_frame * cfg.head_dim;
+  q.kc = L.kc; q.vc = L.vc; q.ks = L.ks; q.vs = L.vs;
+  q.slots_padded = c->plan.slots_padded;
+  q.write_slot = w.write_slot;
+  if (rtv::launch_qkv_gemm_append(q, static_cast<hipStream_t>(stream)) != hipSuccess) return RTV_ERR_HIP;
+  L.appended = 1;
+  return RTV_OK;
+}
+
 rtv_status rtv_device_state_begin(rtv_cache* c, void* stream) {
   if (!c) return RTV_ERR_INVALID_ARG;
   if (c->device_state) return RTV_ERR_STATE;

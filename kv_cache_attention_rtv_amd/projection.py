@@ -1,6 +1,6 @@
 """torch-facing wrappers of the projection entry points (argument marshalling
-only): per-tensor e4m3 quantization and the FP8 GEMM, both run by the library's
-kernels on the given stream."""
+only): per-tensor e4m3 quantization, the FP8 GEMM, and the FP8 QKV GEMM fused
+with the cache upkeep, all run by the library's kernels on the given stream."""
 from __future__ import annotations
 
 import torch
@@ -53,3 +53,28 @@ def gemm_fp8(a: torch.Tensor, sa: torch.Tensor, bt: torch.Tensor, sb: torch.Tens
     abi.rtv_gemm_fp8(a.data_ptr(), sa.data_ptr(), bt.data_ptr(), sb.data_ptr(), out.data_ptr(),
                      M, N, K, out.stride(0), _stream(stream))
     return out
+
+
+def qkv_gemm_append(cache, layer: int, x: torch.Tensor, sx: torch.Tensor, wt: torch.Tensor,
+                    sw: torch.Tensor, q_cols: int, q_out: torch.Tensor | None = None, stream=None):
+    """QKV = sx * sw * X[M][K] @ Wt[N][K]^T with N = q_cols + 2 * n_kv_heads * head_dim:
+    the Q columns into q_out (bf16 [M, q_cols], allocated if None), the K and V
+    heads through RoPE (K) and per-(token, head) e4m3 straight into the layer's
+    ring as the chunk's append.  Returns q_out."""
+    c = cache.cfg
+    if x.dtype != torch.uint8 or wt.dtype != torch.uint8 or x.dim() != 2 or wt.dim() != 2:
+        raise TypeError("x and wt must be 2-D uint8 (e4m3 code) tensors")
+    if not (x.is_contiguous() and wt.is_contiguous()):
+        raise ValueError("x and wt must be contiguous")
+    M, K = x.shape
+    N, K2 = wt.shape
+    if K != K2 or N != q_cols + 2 * c.n_kv_heads * c.head_dim:
+        raise ValueError(f"shapes: x {tuple(x.shape)}, wt {tuple(wt.shape)}, q_cols {q_cols}")
+    if q_cols > 0 and q_out is None:
+        q_out = torch.empty((M, q_cols), dtype=torch.bfloat16, device=x.device)
+    q_ptr, q_stride = (q_out.data_ptr(), q_out.stride(0)) if q_cols > 0 else (0, 0)
+    if q_cols > 0 and (q_out.dtype != torch.bfloat16 or q_out.shape != (M, q_cols) or q_out.stride(1) != 1):
+        raise ValueError("q_out must be a bf16 [M, q_cols] tensor with unit column stride")
+    abi.rtv_qkv_gemm_append(cache.handle, layer, x.data_ptr(), sx.data_ptr(), wt.data_ptr(), sw.data_ptr(),
+                            M, K, q_cols, q_ptr, q_stride, _stream(stream))
+    return q_out
