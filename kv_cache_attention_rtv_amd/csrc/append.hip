@@ -9,7 +9,9 @@
 //
 // One workgroup = one 64-slot tile of the ring x three KV heads (512 threads,
 // 8 lanes per slot).  The RoPE (cos, sin) of a slot is loaded once and
-// applied to the K rows of all three heads.  Eight lanes share a token row: lane g of the row holds the element groups
+// applied to the K rows of all three heads; the heads' K/V pieces are loaded
+// two heads ahead of the arithmetic.  Eight lanes share a token row: lane g of
+// the row holds the element groups
 // [g*E, g*E+E) and [D/2+g*E, D/2+g*E+E), E = D/16, i.e. both halves of its
 // RoPE pairs, so the rotation needs no lane exchange and every bf16 load is
 // 8 lanes x 16 B = 128 B contiguous.  The row amax is an 8-lane DPP max.
@@ -129,15 +131,18 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
   const bool valid = slot >= lo && slot < hi;
   const int64_t t = valid ? slot - a.write_slot : 0;   // token in the chunk
 
-  // ---- issue every global load before any arithmetic: the K and V pieces of
-  // the group's heads and, once for all of them, the row's RoPE (cos, sin) ----
+  // ---- global loads ahead of the arithmetic: the K and V pieces of the first
+  // two heads and, once for all heads, the row's RoPE (cos, sin); the pieces
+  // of head j + 2 are loaded once head j is done, so at most two heads' pieces
+  // are live (79 VGPRs: three workgroups per CU, the whole chunk in one round)
   RowPiece<E> kp[HPW], vp[HPW];
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
+  auto load_head = [&](int j) {
     const bool hv = h0 + j < a.n_heads;
     kp[j] = load_piece<D>(a.k + t * a.ldk + (int64_t)(h0 + j) * D, g, valid && hv);
     vp[j] = load_piece<D>(a.v + t * a.ldv + (int64_t)(h0 + j) * D, g, valid && hv);
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < (HPW < 2 ? HPW : 2); ++j) load_head(j);
   float4 cs[E / 2];
   {
     const float4* tab = (const float4*)(a.rope + (t * HALF + g * E) * 2);
@@ -212,6 +217,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
       }
       if (valid && g == 0) a.vs[(int64_t)h * a.slots_padded + slot] = q.s;
     }
+    if (j + 2 < HPW) load_head(j + 2);
   }
   __syncthreads();
 
