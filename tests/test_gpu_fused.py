@@ -132,3 +132,40 @@ def test_fused_projection_size_sampled(rtv_lib):
     positions = orope.chunk_positions(0, wl.chunk_frames, wl.tokens_per_frame)
     print("fused projection size", flush=True)
     _run(rtv_lib, cache, 0, xc, sx, wc, sw, q_cols, rows, positions, cfg.rope_base)
+
+
+def test_fused_argument_errors(rtv_lib):
+    """Shapes the fused projection rejects before enqueuing anything."""
+    wl = get_workload("tiny")
+    cfg = rtv_lib.RtvConfig(1, 2, wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame, wl.chunk_frames,
+                            wl.capacity_frames, 2 * wl.chunk_frames)
+    c = rtv_lib.RtvCache(cfg)
+    abi = rtv_lib.abi
+    n, D, H = wl.chunk_tokens, wl.head_dim, wl.n_kv_heads
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    kv = 2 * H * D
+
+    def call(n_tok, k_dim, q_cols, q_ptr=None):
+        x = torch.zeros((max(n_tok, 1), k_dim), dtype=torch.uint8, device="cuda")
+        w = torch.zeros((q_cols + kv, k_dim), dtype=torch.uint8, device="cuda")
+        q = torch.empty((max(n_tok, 1), max(q_cols, 8)), dtype=torch.bfloat16, device="cuda")
+        abi.rtv_qkv_gemm_append(c.handle, 0, x.data_ptr(), one.data_ptr(), w.data_ptr(), one.data_ptr(),
+                                n_tok, k_dim, q_cols, q.data_ptr() if q_ptr is None else q_ptr, q.stride(0), 0)
+
+    for args, status in (((n - 1, 64, 0), abi.RTV_ERR_INVALID_ARG),      # not one chunk
+                         ((n, 60, 0), abi.RTV_ERR_INVALID_ARG),          # k_dim not a multiple of 64
+                         ((n, 64, D + 1), abi.RTV_ERR_INVALID_ARG)):     # Q columns not whole heads
+        with pytest.raises(rtv_lib.RtvError) as e:
+            call(*args)
+        assert e.value.status == status, args
+    with pytest.raises(rtv_lib.RtvError) as e:
+        call(n, 64, D, q_ptr=0)                                          # Q columns without an output
+    assert e.value.status == abi.RTV_ERR_INVALID_ARG
+    assert c.layout(0).appended == 0
+    call(n, 64, 0)                                                      # valid: counts as the append
+    c.advance(0)
+    call(n, 64, 0)
+    c.advance(0)
+    with pytest.raises(rtv_lib.RtvError) as e:                          # RoPE table holds 2 chunks
+        call(n, 64, 0)
+    assert e.value.status == abi.RTV_ERR_STATE

@@ -8,7 +8,6 @@ step after step with new inputs.  Every replay is checked against an eager
 host-state run of the same inputs, with eager work and synchronizations
 between the replays.
 """
-import numpy as np
 import pytest
 import torch
 
@@ -169,3 +168,29 @@ def test_device_state_rope_exhaustion(rtv_lib):
     with pytest.raises(rtv_lib.RtvError) as e:
         c.device_state_end()
     assert e.value.status == rtv_lib.abi.RTV_ERR_STATE
+
+
+def test_device_state_call_order_errors(rtv_lib):
+    """begin twice, end without begin, and the fused projection (host-state
+    only) inside the mode are STATE / UNSUPPORTED errors that change nothing."""
+    wl = get_workload("tiny")
+    cfg = _cfg(rtv_lib, wl, 1, 4 * wl.chunk_frames)
+    c = rtv_lib.RtvCache(cfg)
+    abi = rtv_lib.abi
+    with pytest.raises(rtv_lib.RtvError) as e:
+        c.device_state_end()
+    assert e.value.status == abi.RTV_ERR_STATE
+    c.device_state_begin()
+    with pytest.raises(rtv_lib.RtvError) as e:
+        c.device_state_begin()
+    assert e.value.status == abi.RTV_ERR_STATE
+    n = wl.chunk_tokens
+    x = torch.zeros((n, 64), dtype=torch.uint8, device="cuda")
+    cols = 2 * wl.n_kv_heads * wl.head_dim
+    w = torch.zeros((cols, 64), dtype=torch.uint8, device="cuda")
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(rtv_lib.RtvError) as e:
+        rtv_lib.qkv_gemm_append(c, 0, x, one, w, one, 0)
+    assert e.value.status == abi.RTV_ERR_UNSUPPORTED
+    c.device_state_end()
+    assert c.layout(0).next_global_frame == 0
