@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--workload", choices=["step", "projection"], default="step",
                    help="projection: time the projection workload's chunk (per-tensor e4m3 of X, the FP8 "
                         "QKV GEMM and the append) unfused and fused, one JSON line")
+    p.add_argument("--no-growth", action="store_true",
+                   help="fill the rings with appends only instead of timing the four window-growth steps "
+                        "(the profiler runs use it, so that every attention dispatch sees the full window)")
     p.add_argument("--call-steps", type=int, default=2,
                    help="eager steps with HIP events around every call, for the per-call figures")
     p.add_argument("--cpu-heads", type=int, default=8,
@@ -368,11 +371,24 @@ def main():
         cache.advance(-1, stream=stream)
 
     # steady state: fill every layer's ring before the warm-up, so every timed
-    # (and warm-up) attend sees the full window
+    # (and warm-up) attend sees the full window.  By default the filling steps
+    # are whole steps, timed one by one: the windows of a fresh cache grow
+    # 4, 8, 12, 16 frames over them.
+    growth = []
     for _ in range(wl.capacity_frames // wl.chunk_frames):
-        for layer in range(wl.n_layers):
-            cache.append(layer, inputs[layer][1], inputs[layer][2], stream=stream)
-        cache.advance(-1, stream=stream)
+        if args.no_growth:
+            for layer in range(wl.n_layers):
+                cache.append(layer, inputs[layer][1], inputs[layer][2], stream=stream)
+            cache.advance(-1, stream=stream)
+            continue
+        wf = cache.window(0).window_frames
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run_step()
+        b.record(stream)
+        growth.append((wf, a, b))
+    torch.cuda.synchronize()
+    growth = [(wf, a.elapsed_time(b)) for wf, a, b in growth]
     windows = []
     for s in range(args.warmup):
         run_step()
@@ -400,6 +416,7 @@ def main():
         run_step(ev)
     eager_ms, eager_wall = timed(n_call_steps, eager_step)
     mode = "eager launches"
+    per_step = None
     if args.eager:
         gpu_ms, wall = eager_ms, eager_wall
     else:
@@ -420,7 +437,16 @@ def main():
         torch.cuda.synchronize()
         for _ in range(args.warmup):
             graph.replay()
-        gpu_ms, wall = timed(args.steps, graph.replay)
+        step_events = []
+
+        def replay():
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+            step_events.append((a, b))
+        gpu_ms, wall = timed(args.steps, replay)
+        per_step = sorted(a.elapsed_time(b) for a, b in step_events)
         cache.device_state_end(stream=stream)
         windows.append(cache.window(0).window_frames)
         mode = "one HIP graph per step (device-resident ring state), replayed"
@@ -471,6 +497,10 @@ def main():
             "parallelism": "none (one GPU's head share)", "launch": mode,
         },
         "eager_ms_per_step": round(eager_ms / n_call_steps, 3),
+        "step_ms_median_min": ([round(per_step[len(per_step) // 2], 3), round(per_step[0], 3)]
+                               if per_step else None),
+        "growth_steps_ms": [{"window_frames": wf, "ms": round(ms, 3)} for wf, ms in growth] or None,
+        "tokens_appended_per_s": round(wl.calls_per_layer * wl.n_layers * n / (ms_per_step * 1e-3)),
         "roofline": {
             "bound": "mfma",
             "kernel": ("rtv_attend = factors_kernel + attend_kernel<128, false, false, false> + "
