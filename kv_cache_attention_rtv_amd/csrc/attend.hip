@@ -61,7 +61,10 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 #endif
 constexpr int kWaves = RTV_ATTEND_WAVES;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kQPB = 256;                   // queries per workgroup
+#ifndef RTV_ATTEND_QPB
+#define RTV_ATTEND_QPB 256
+#endif
+constexpr int kQPB = RTV_ATTEND_QPB;        // queries per workgroup
 constexpr int kQPW = kQPB / kWaves;         // queries per wave
 constexpr int kSub = kQPW / 32;             // 32-query sub-tiles per wave (they share the K/V operands)
 constexpr int kStages = 4;                  // LDS ring: tiles it - 1 .. it + 2
@@ -892,47 +895,52 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
 
 // Merge the key-range parts of the split units: for each query,
 // M = max_p m_p, w_p = 2^(m_p - M), O = sum_p w_p O_p / sum_p w_p l_p.
+// One workgroup = kCombineQ queries of one split unit (blockIdx.x: the unit,
+// blockIdx.y: the query group), kCombineT threads per query with D /
+// kCombineT dimensions each: a query's partial rows are read as contiguous
+// runs and the whole device takes part.
+constexpr int kCombineQ = 16;
+constexpr int kCombineT = 16;
 template <int D>
-__global__ __launch_bounds__(2 * kQPB) void combine_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kCombineQ * kCombineT) void combine_kernel(AttendArgs a) {
   if (a.dstate && !attend_derive(a)) return;
+  constexpr int DT = D / kCombineT;               // dimensions per thread
   const int r = blockIdx.x;                       // split unit r
   if (a.n_full + r >= a.n_work) return;           // (device-state grids cover the most split units)
   const int unit = a.n_full + r;
   const int head = unit / a.n_qtiles;
   const int qtile = unit % a.n_qtiles;
   const int S = a.parts_per_unit;
-  const int q = threadIdx.x >> 1;                 // 2 threads per query
-  const int dh = (threadIdx.x & 1) * (D / 2);
+  const int q = blockIdx.y * kCombineQ + (int)threadIdx.x / kCombineT;
+  const int d0 = ((int)threadIdx.x % kCombineT) * DT;
   const int row = qtile * kQPB + q;
-  if (q >= kQPB || row >= a.n_tokens) return;
+  if (row >= a.n_tokens) return;
   const int j0 = r * S;
   float M = -INFINITY;
   for (int p = 0; p < S; ++p) M = fmaxf(M, a.ws_ml[((int64_t)(j0 + p) * kQPB + q) * 2]);
   float L = 0.0f;
-  float acc[D / 2];
+  float acc[DT];
 #pragma unroll
-  for (int d = 0; d < D / 2; ++d) acc[d] = 0.0f;
+  for (int d = 0; d < DT; ++d) acc[d] = 0.0f;
   for (int p = 0; p < S; ++p) {
     const float2 ml = *(const float2*)(a.ws_ml + ((int64_t)(j0 + p) * kQPB + q) * 2);
     const float w = exp2f(ml.x - M);
     L += w * ml.y;
-    const float* po = a.ws_o + ((int64_t)(j0 + p) * kQPB + q) * D + dh;
+    const float* po = a.ws_o + ((int64_t)(j0 + p) * kQPB + q) * D + d0;
 #pragma unroll
-    for (int d = 0; d < D / 2; d += 4) {
+    for (int d = 0; d < DT; d += 4) {
       const float4 o = *(const float4*)(po + d);
       acc[d] += w * o.x; acc[d + 1] += w * o.y; acc[d + 2] += w * o.z; acc[d + 3] += w * o.w;
     }
   }
   const float inv = 1.0f / L;
-  uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D + dh;
+  uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D + d0;
 #pragma unroll
-  for (int d = 0; d < D / 2; d += 8) {
-    uint4 w;
+  for (int d = 0; d < DT; d += 4) {
+    uint2 w;
     w.x = pack_bf16x2(acc[d] * inv, acc[d + 1] * inv);
     w.y = pack_bf16x2(acc[d + 2] * inv, acc[d + 3] * inv);
-    w.z = pack_bf16x2(acc[d + 4] * inv, acc[d + 5] * inv);
-    w.w = pack_bf16x2(acc[d + 6] * inv, acc[d + 7] * inv);
-    *(uint4*)(dst + d) = w;
+    *(uint2*)(dst + d) = w;
   }
 }
 
@@ -1035,10 +1043,11 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
 #undef RTV_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || rem == 0) return e;
+  const dim3 cg(rem, kQPB / kCombineQ), cb(kCombineQ * kCombineT);
   if (head_dim == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, dim3(rem), dim3(2 * kQPB), 0, stream, args);
+    hipLaunchKernelGGL(combine_kernel<128>, cg, cb, 0, stream, args);
   else
-    hipLaunchKernelGGL(combine_kernel<64>, dim3(rem), dim3(2 * kQPB), 0, stream, args);
+    hipLaunchKernelGGL(combine_kernel<64>, cg, cb, 0, stream, args);
   return hipGetLastError();
 }
 
