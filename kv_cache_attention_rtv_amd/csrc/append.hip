@@ -22,7 +22,9 @@
 // Arithmetic is fixed bit for bit: RoPE products and the sum/difference are
 // rounded separately (no contraction: this file is built with
 // -ffp-contract=off), scale = RN(amax/448), x/scale is the correctly rounded
-// quotient (div_rn), and the e4m3 conversion rounds to nearest even.
+// quotient, and the e4m3 conversion rounds to nearest even.  Rows with a
+// normal scale (all of them in practice) take the short form of these steps
+// (quant_row); the others the general one.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "ring.hpp"
@@ -32,6 +34,8 @@ namespace {
 
 constexpr int kAppendThreads = 512;   // 8 lanes per slot of a 64-slot tile
 constexpr int kAppendHeads = 3;       // KV heads per workgroup (share the RoPE loads)
+// (six waves per SIMD, at most 80 VGPRs: three workgroups per CU, the step
+// chunk's 748 in one round)
 
 __device__ __forceinline__ float dpp_max8(float x) {
   // max over the 8 lanes of each row group: quad xor 1, quad xor 2, then the
@@ -106,7 +110,7 @@ __device__ __forceinline__ bool append_derive(AppendArgs& a, int groups) {
 }
 
 template <int D, int HPW>
-__global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(AppendArgs a) {
+__global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(6))) void append_rope_quant_kernel(AppendArgs a) {
   constexpr int E = D / 16;          // elements per lane per half
   constexpr int HALF = D / 2;
   constexpr int LDS_STRIDE = D + 4;  // bytes per V row in LDS
@@ -155,6 +159,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
     const int h = h0 + j;
     if (h >= a.n_heads) break;                   // uniform over the workgroup
     // ---- K: rotate, quantize, store ------------------------------------
+    // (each part takes the short form when every valid row of the wave has a
+    // normal scale: one uniform choice per part)
     {
       float r0[E], r1[E];
       float amax = 0.0f;
@@ -174,48 +180,44 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_quant_kernel(Appen
           const float b1 = x0 * si;
           r0[e] = a0 - b0;
           r1[e] = a1 + b1;
-          amax = fmaxf(amax, fmaxf(fabsf(r0[e]), fabsf(r1[e])));
+          amax = fmaxf(fmaxf(amax, fabsf(r0[e])), fabsf(r1[e]));
         }
       }
       amax = dpp_max8(amax);
-      const RowQuant q = row_quant(amax);
+      uint32_t c0[E / 4], c1[E / 4];
+      const float ks = quant_row<E>(r0, r1, c0, c1, amax, __all(!valid || fast_amax(amax)));
       if (valid) {
         uint8_t* dst = a.kc + ((int64_t)h * a.slots_padded + slot) * D;
         if constexpr (E == 8) {
-          uint2 c0, c1;
-          c0.x = quant4(r0[0], r0[1], r0[2], r0[3], q);
-          c0.y = quant4(r0[4], r0[5], r0[6], r0[7], q);
-          c1.x = quant4(r1[0], r1[1], r1[2], r1[3], q);
-          c1.y = quant4(r1[4], r1[5], r1[6], r1[7], q);
-          *(uint2*)(dst + g * E) = c0;
-          *(uint2*)(dst + HALF + g * E) = c1;
+          *(uint2*)(dst + g * E) = make_uint2(c0[0], c0[1]);
+          *(uint2*)(dst + HALF + g * E) = make_uint2(c1[0], c1[1]);
         } else {
-          *(uint32_t*)(dst + g * E) = quant4(r0[0], r0[1], r0[2], r0[3], q);
-          *(uint32_t*)(dst + HALF + g * E) = quant4(r1[0], r1[1], r1[2], r1[3], q);
+          *(uint32_t*)(dst + g * E) = c0[0];
+          *(uint32_t*)(dst + HALF + g * E) = c1[0];
         }
-        if (g == 0) a.ks[(int64_t)h * a.slots_padded + slot] = q.s;
+        if (g == 0) a.ks[(int64_t)h * a.slots_padded + slot] = ks;
       }
     }
     // ---- V: quantize, stage row-major in LDS ----------------------------
     {
       float x0[E], x1[E];
+      float amax = 0.0f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         x0[e] = (e & 1) ? bf16_hi(vp[j].w0[e >> 1]) : bf16_lo(vp[j].w0[e >> 1]);
         x1[e] = (e & 1) ? bf16_hi(vp[j].w1[e >> 1]) : bf16_lo(vp[j].w1[e >> 1]);
+        amax = fmaxf(fmaxf(amax, fabsf(x0[e])), fabsf(x1[e]));
       }
-      float amax = 0.0f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) amax = fmaxf(amax, fmaxf(fabsf(x0[e]), fabsf(x1[e])));
       amax = dpp_max8(amax);
-      const RowQuant q = row_quant(amax);
+      uint32_t c0[E / 4], c1[E / 4];
+      const float vs = quant_row<E>(x0, x1, c0, c1, amax, __all(!valid || fast_amax(amax)));
       uint32_t* row = vrow[j] + r * (LDS_STRIDE / 4);
 #pragma unroll
       for (int i = 0; i < E / 4; ++i) {
-        row[(g * E) / 4 + i] = quant4(x0[4 * i], x0[4 * i + 1], x0[4 * i + 2], x0[4 * i + 3], q);
-        row[(HALF + g * E) / 4 + i] = quant4(x1[4 * i], x1[4 * i + 1], x1[4 * i + 2], x1[4 * i + 3], q);
+        row[(g * E) / 4 + i] = c0[i];
+        row[(HALF + g * E) / 4 + i] = c1[i];
       }
-      if (valid && g == 0) a.vs[(int64_t)h * a.slots_padded + slot] = q.s;
+      if (valid && g == 0) a.vs[(int64_t)h * a.slots_padded + slot] = vs;
     }
     if (j + 2 < HPW) load_head(j + 2);
   }

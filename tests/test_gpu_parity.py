@@ -268,3 +268,55 @@ def test_stress_outliers_zero_rows_window_cycle(rtv_lib):
             print(f"stress step={step} window={maxw} normalised worst so far max={worst[0]:.3e} mean={worst[1]:.3e}", flush=True)
         gpu.advance(0)
         ora.advance(0)
+
+
+@pytest.mark.parametrize("D,H", [(128, 4), (64, 3)])
+def test_append_extreme_row_magnitudes(rtv_lib, D, H):
+    """Rows whose magnitudes reach the ends of the float range: scales of
+    2^-89 (just inside the short form of the quantization, which needs amax >=
+    448 * 2^-100), 2^-93 (either side of that bound), 2^-120, 2^-128 and 2^-133
+    (subnormal bf16 values), 2^100 and 2^125 (near the bf16 maximum), all-zero
+    rows, and rows of -0.0 with one nonzero value (signed zeros in a row with
+    a normal scale).  Per (token, head) classes: in blocks of 8 tokens (one
+    wave of the append holds 8 rows) over the first half of the chunk, so that
+    whole waves take one form, and at random over the second half, so that
+    waves mix them.  Codes and scales bit-exact against the oracle."""
+    from workloads.generate import bf16_bits_to_f32, f32_to_bf16_bits
+    wl = dataclasses.replace(get_workload("tiny"), head_dim=D, n_kv_heads=H, n_q_heads=H)
+    gpu, ora = _caches(rtv_lib, wl, max_global_frames=4 * wl.chunk_frames)
+    exps = [0, -89, -93, -120, -128, -133, 100, 125]
+    n_cls = len(exps) + 2
+    n = wl.chunk_tokens
+    for step in range(3):
+        _, k, v = qkv_normal(wl, 0, step, 0)
+        rng = np.random.default_rng([11, D, step])
+        tok = np.arange(n)
+        cls_t = np.where(tok < n // 2, (tok // 8) % n_cls, rng.integers(0, n_cls, n))
+        cls = (cls_t[:, None] + np.arange(H)[None, :]) % n_cls          # [n, H]
+
+        def shape_rows(bits, salt):
+            x = bf16_bits_to_f32(bits).astype(np.float64)
+            out = np.zeros_like(x)
+            for c, e in enumerate(exps):
+                m = cls == c
+                out[m] = x[m] * 2.0 ** e
+            negz = cls == len(exps) + 1
+            out[negz] = -0.0
+            ti, hi = np.nonzero(negz)
+            out[ti, hi, (ti * 7 + hi + salt) % D] = x[ti, hi, 0]
+            return f32_to_bf16_bits(out.astype(np.float32)).reshape(bits.shape)
+
+        k2, v2 = shape_rows(k, 0), shape_rows(v, 3)
+        print(f"extreme magnitudes D={D} step={step}", flush=True)
+        gpu.append(0, to_dev_bf16(k2), to_dev_bf16(v2))
+        e = ora.append(0, k2, v2)
+        L = gpu.layout(0)
+        slots = L.head_frame * wl.tokens_per_frame + tok
+        gk, gks, gv, gvs = ring_rows(gpu, 0, slots)
+        for what, got, want in (("K codes", gk, e.k_codes), ("V codes", gv, e.v_codes),
+                                ("K scales", gks.view(np.uint32), e.k_scales.view(np.uint32)),
+                                ("V scales", gvs.view(np.uint32), e.v_scales.view(np.uint32))):
+            bad = np.argwhere(got != want)
+            assert bad.size == 0, (what, step, bad[:4].tolist(), [int(cls[t, h]) for t, h, *_ in bad[:4]])
+        gpu.advance(0)
+        ora.advance(0)
