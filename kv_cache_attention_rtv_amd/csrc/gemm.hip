@@ -112,18 +112,33 @@ quant_apply_kernel(const uint16_t* __restrict__ x, int64_t n, const uint32_t* __
   uint32_t m = 0;
   for (int i = threadIdx.x; i < n_partial; i += kQuantThreads) m = max(m, partial[i]);
   m = block_max(m, red);
-  const RowQuant q = row_quant(__uint_as_float(m << 16));
+  const float amax = __uint_as_float(m << 16);
+  const RowQuant q = row_quant(amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale = q.s;
   const int64_t n8 = n >> 3;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint2* cv = reinterpret_cast<uint2*>(codes);
   const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n8; i += stride) {
-    const uint4 w = xv[i];
-    uint2 o;
-    o.x = quant4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), q);
-    o.y = quant4(bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w), q);
-    cv[i] = o;
+  if (fast_amax(amax)) {
+    // the short form of the quantization (same codes; the scale q.s equals
+    // scale448(amax) in this range)
+    const float fs = scale448(amax);
+    const float fr = 1.0f / fs;
+    for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n8; i += stride) {
+      const uint4 w = xv[i];
+      uint2 o;
+      o.x = quant4_fast(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), fs, fr);
+      o.y = quant4_fast(bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w), fs, fr);
+      cv[i] = o;
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n8; i += stride) {
+      const uint4 w = xv[i];
+      uint2 o;
+      o.x = quant4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y), q);
+      o.y = quant4(bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w), q);
+      cv[i] = o;
+    }
   }
   if (blockIdx.x == 0)
     for (int64_t i = (n8 << 3) + threadIdx.x; i < n; i += kQuantThreads)
@@ -277,6 +292,9 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
       __syncthreads();
       amax = fmaxf(amax, amax_x[(wave ^ 1) * 64 + lane]);
     }
+    // rows with a normal scale take the short form of the quantization (one
+    // uniform choice per wave, taken before the lanes of other rows leave)
+    const bool fast = __all(!valid || !in_range || fast_amax(amax));
     if (!valid || !in_range) continue;
     if (is_q) {
       uint16_t* dst = g.c + (int64_t)m * g.ldc + col + 32 * part;
@@ -292,13 +310,8 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
       }
       continue;
     }
-    const RowQuant rq = row_quant(amax);
     uint32_t c0[8], c1[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      c0[q] = quant4(x0[4 * q], x0[4 * q + 1], x0[4 * q + 2], x0[4 * q + 3], rq);
-      c1[q] = quant4(x1[4 * q], x1[4 * q + 1], x1[4 * q + 2], x1[4 * q + 3], rq);
-    }
+    const float row_s = quant_row<32>(x0, x1, c0, c1, amax, fast);
     const int64_t slot = g.write_slot + m;
     if (is_k) {
       const int h = (col - g.q_cols) / D;
@@ -307,7 +320,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
       *reinterpret_cast<uint4*>(dst + 16) = make_uint4(c0[4], c0[5], c0[6], c0[7]);
       *reinterpret_cast<uint4*>(dst + HALF) = make_uint4(c1[0], c1[1], c1[2], c1[3]);
       *reinterpret_cast<uint4*>(dst + HALF + 16) = make_uint4(c1[4], c1[5], c1[6], c1[7]);
-      if (part == 0) g.ks[(int64_t)h * g.slots_padded + slot] = rq.s;
+      if (part == 0) g.ks[(int64_t)h * g.slots_padded + slot] = row_s;
     } else {
       // transposed V tile: byte vt_pos(slot % 64) of row d; the wave's 64
       // lanes fill one 64-byte row per d
@@ -319,7 +332,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
         vt[(int64_t)(32 * part + q) * kTileKeys] = (uint8_t)(c0[q >> 2] >> (8 * (q & 3)));
         vt[(int64_t)(HALF + 32 * part + q) * kTileKeys] = (uint8_t)(c1[q >> 2] >> (8 * (q & 3)));
       }
-      if (part == 0) g.vs[(int64_t)h * g.slots_padded + slot] = rq.s;
+      if (part == 0) g.vs[(int64_t)h * g.slots_padded + slot] = row_s;
     }
   }
 }

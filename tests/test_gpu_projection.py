@@ -69,7 +69,7 @@ def _random_codes(rng, shape):
 
 @pytest.mark.parametrize("n,kind", [(1, "normal"), (7, "normal"), (8, "normal"), (1000, "normal"),
                                     (4097 * 8 + 3, "normal"), (300001, "outlier"), (4099, "zero"),
-                                    (2051, "tiny")])
+                                    (2051, "tiny"), (2053, "huge"), (4101, "negzero")])
 def test_quant_per_tensor_matches_oracle(rtv_lib, n, kind):
     rng = np.random.default_rng(n)
     x = rng.standard_normal(n).astype(np.float32)
@@ -80,6 +80,10 @@ def test_quant_per_tensor_matches_oracle(rtv_lib, n, kind):
         x[::3] = -0.0
     elif kind == "tiny":
         x *= np.float32(1e-37)
+    elif kind == "huge":
+        x *= np.float32(1e37)                  # amax near the bf16 maximum
+    elif kind == "negzero":
+        x[::5] = -0.0                          # signed zeros under a normal scale
     bits = obf16.from_f64(x.astype(np.float64))
     print(f"quant n={n} kind={kind}", flush=True)
     codes, scale = rtv_lib.quant_fp8_per_tensor(to_dev_bf16(bits))
