@@ -72,6 +72,7 @@ def parse():
 
 
 KERNEL_SOURCES = {
+    "attend16_kernel": "kv_cache_attention_rtv_amd/csrc/attend.hip",
     "attend_kernel": "kv_cache_attention_rtv_amd/csrc/attend.hip",
     "combine_kernel": "kv_cache_attention_rtv_amd/csrc/attend.hip",
     "factors_kernel": "kv_cache_attention_rtv_amd/csrc/attend.hip",
@@ -464,7 +465,7 @@ def main():
 
     # HBM bytes per rtv_attend call (attention + combine kernels of the
     # steady-state window) and per append, from the calibrated counters
-    att_traffic = traffic_of(args.traffic_json, "attend_kernel<128, false, false, false>")
+    att_traffic = traffic_of(args.traffic_json, "attend16_kernel<false, false, false>")
     comb_traffic = traffic_of(args.traffic_json, "combine_kernel<128>")
     fac_traffic = traffic_of(args.traffic_json, "factors_kernel")
     app_traffic = traffic_of(args.traffic_json, "append_rope_quant_kernel<128")
@@ -503,7 +504,7 @@ def main():
         "tokens_appended_per_s": round(wl.calls_per_layer * wl.n_layers * n / (ms_per_step * 1e-3)),
         "roofline": {
             "bound": "mfma",
-            "kernel": ("rtv_attend = factors_kernel + attend_kernel<128, false, false, false> + "
+            "kernel": ("rtv_attend = factors_kernel + attend16_kernel<false, false, false> + "
                        "combine_kernel<128>"),
             "achieved": round(att_tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic,

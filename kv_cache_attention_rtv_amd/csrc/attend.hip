@@ -16,11 +16,15 @@
 // barrier per tile; waves 0-3 stage the K rows and waves 4-7 the V rows of
 // tile t+2 while tile t is computed.
 //
-// Per wave and tile, with v_mfma_f32_32x32x64_f8f6f4 (e4m3, f32 accumulate):
-//   S^T[key][query] = K . Q^T + C_key     2 key halves x D/64 k-steps
-//   lane (hh, i) holds query i and 32 of the 64 keys: the softmax row is
-//   per lane plus one v_permlane32_swap with lane i^32;
-//   O^T[d][query] += V^T . P'^T           D/32 d sub-tiles
+// Per wave and tile (e4m3 operands, f32 accumulate):
+//   S^T[key][query] = K . Q^T + C_key     head dim 64 (attend_kernel): with
+//   v_mfma_f32_32x32x64_f8f6f4, 2 key halves x D/64 k-steps; lane (hh, i)
+//   holds query i and 32 of the 64 keys: the softmax row is per lane plus one
+//   v_permlane32_swap with lane i^32.  Head dim 128 (attend16_kernel): with
+//   v_mfma_f32_16x16x128_f8f6f4, 4 key blocks x 2 query blocks; a lane holds
+//   16 keys of 2 queries, which halves its per-key factor reads, and P' is
+//   brought to the PV operand layout by v_permlane16_swap (see there);
+//   O^T[d][query] += V^T . P'^T           D/32 d sub-tiles (32x32x64)
 //   L[r][query]   += U . P'^T             one product: the row sum
 // Scores: the queries of a workgroup share one e4m3 scale s_q, so the whole
 // per-score scale folds into a per-key factor kf = sk * s_q * log2(e)/sqrt(D).
@@ -893,6 +897,471 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   }
 }
 
+// ---- head dim 128: scores by v_mfma_f32_16x16x128_f8f6f4 -------------------
+// The same computation as attend_kernel<128, ...> with the score products taken
+// 16 keys x 16 queries at a time over the whole head dimension.  Lane (q4 =
+// lane / 16, i = lane % 16) then holds, for each of the tile's four 16-key
+// blocks kb and the wave's two 16-query blocks qb, the scores of keys
+// key16(kb, 4 q4 + e) (e = 0..3) for query 16 qb + i: 16 keys x 2 queries,
+// against 32 keys x 1 query with the 32x32x64 product, so that a lane reads
+// half as many per-key factors (kf, C) from LDS.  One v_permlane16_swap per
+// pair of P' dwords (query blocks 0 and 1 of one key block) then gives every
+// lane the 32 codes of one query in the B-operand order of the PV product:
+// key16 maps (block, row) to keys so that code byte p of a lane holds the key
+// that the transposed V rows keep at position p.  The running max is kept per
+// query block; its rare updates reduce over the four lanes of a query.
+__device__ __forceinline__ int key16(int kb, int r) { return vt_key(16 * (r >> 2) + 4 * kb + (r & 3)); }
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4f mfma16_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma16_fp8_bscaled(const v8i& a, const v8i& b, const v4f& c, int e) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, e);
+}
+// max over the four lanes i, i + 16, i + 32, i + 48 (the lanes of one query)
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// max of the 16 scores of one query block
+__device__ __forceinline__ float max16(const float (&t)[4][4]) {
+  float a[6];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int j = 3 * i;
+    a[i] = __builtin_fmaxf(__builtin_fmaxf(t[j >> 2][j & 3], t[(j + 1) >> 2][(j + 1) & 3]), t[(j + 2) >> 2][(j + 2) & 3]);
+  }
+  a[5] = t[3][3];
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(a[0], a[1]), a[2]),
+                         __builtin_fmaxf(__builtin_fmaxf(a[3], a[4]), a[5]));
+}
+
+template <bool MASK, bool QLO, bool PLO>
+__global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kernel(AttendArgs a) {
+  static_assert(kSub == 1, "one 32-query sub-tile per wave");
+  constexpr int D = 128;
+  if (a.dstate && !attend_derive(a)) return;
+  using SM = Smem<D>;
+  using LU = LogUnits<PLO>;
+  constexpr int NDT = D / 32;               // 32-row d sub-tiles of O^T
+  constexpr int P = D / 4;                  // RoPE pairs per lane
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * SM::STAGE];
+  __shared__ float red[kWaves];
+
+  // work item: a whole unit (query tile x head) or one key-range part of one
+  const int xcd = blockIdx.x & 7;
+  const int local = blockIdx.x >> 3;
+  int unit, part;
+  if (local < a.full_per_xcd) {
+    unit = xcd * a.full_per_xcd + local;
+    if (unit >= a.n_full) return;
+    part = -1;
+  } else {
+    const int j = xcd * a.parts_per_xcd + (local - a.full_per_xcd);
+    if (j >= a.n_parts) return;
+    unit = a.n_full + j / a.parts_per_unit;
+    part = j;
+  }
+  const int head = unit / a.n_qtiles;
+  const int qtile = unit % a.n_qtiles;
+  const int kvh = head / a.group;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int hh = lane >> 5;
+  const int li = lane & 31;
+  const int q4 = lane >> 4;
+  const int i16 = lane & 15;
+
+  const int64_t Sp = a.slots_padded;
+  const uint8_t* kc = a.kc + (int64_t)kvh * Sp * D;
+  const uint8_t* vc = a.vc + (int64_t)kvh * Sp * D;
+  const uint8_t* frec = (const uint8_t*)a.fac_l + (int64_t)kvh * a.ring_tiles * 1024;
+  const uint8_t* fu = a.fac_u + (int64_t)kvh * a.ring_tiles * 128;
+  const int side = kStageJobs == 1 ? (__builtin_amdgcn_readfirstlane(tid) >= 256 ? 1 : 0) : -1;
+  const int k_off = k_code_off<D>(tid & 255), v_off = v_code_off<D>(tid & 255);
+  const int xk_off = (tid & 63) * 16, xv_off = (tid & 7) * 16;
+
+  // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
+  const int wrow = qtile * kQPB + wave * kQPW;  // first query row of the wave
+  float qamax = 0.0f;
+  {
+    const int row = wrow + li;
+    const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
+    const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
+    const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
+#pragma unroll
+    for (int j = 0; j < P; j += 8) {
+      const uint4 w0 = *(const uint4*)(q_src + P * hh + j);
+      const uint4 w1 = *(const uint4*)(q_src + D / 2 + P * hh + j);
+      const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
+      const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
+        const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
+        const float2 c = *(const float2*)(q_cs + 2 * (j + e));
+        const float r0 = x0 * c.x - x1 * c.y;
+        const float r1 = x1 * c.x + x0 * c.y;
+        qamax = __builtin_fmaxf(qamax, __builtin_fmaxf(fabsf(r0), fabsf(r1)));
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) qamax = __builtin_fmaxf(qamax, __shfl_xor(qamax, o));
+  if (lane == 0) red[wave] = qamax;
+  __syncthreads();
+  qamax = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) qamax = __builtin_fmaxf(qamax, red[w]);
+  const float q_inv = qamax > 0.0f ? kFp8Max / qamax : 0.0f;
+  const float kscale = __builtin_fmaxf((qamax / kFp8Max) * (kLog2e / sqrtf((float)D)), kScaleMin);
+  const float inv_kscale = 1.0f / kscale;
+  const float kscale_u = kscale * LU::kUnit;  // kf in the score units (C stays in raw units)
+
+  // ---- Q prologue pass 2: e4m3 codes in the 16x16x128 B-operand layout ------
+  // lane (q4, i), query block qb: query 16 qb + i, byte b <-> d = 32 q4 + b
+  // (q4 & 1 selects the RoPE pair block, q4 >> 1 the half of the pair)
+  v8i qop[2], qlo[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = wrow + 16 * qb + i16;
+    const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
+    const int pb = q4 & 1;
+    const bool upper = q4 >= 2;
+    const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
+    const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * pb) * 2;
+    float v[P];
+#pragma unroll
+    for (int j = 0; j < P; j += 8) {
+      const uint4 w0 = *(const uint4*)(q_src + P * pb + j);
+      const uint4 w1 = *(const uint4*)(q_src + D / 2 + P * pb + j);
+      const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
+      const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
+        const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
+        const float2 c = *(const float2*)(q_cs + 2 * (j + e));
+        const float r0 = (x0 * c.x - x1 * c.y) * q_inv;
+        const float r1 = (x1 * c.x + x0 * c.y) * q_inv;
+        v[j + e] = upper ? r1 : r0;
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      uint32_t c = 0, lo = 0;
+      if constexpr (QLO) {
+        split_fp8x2<false>(v[4 * w], v[4 * w + 1], c, lo);
+        split_fp8x2<true>(v[4 * w + 2], v[4 * w + 3], c, lo);
+      } else {
+        c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w], v[4 * w + 1], 0, false);
+        c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * w + 2], v[4 * w + 3], (int)c, true);
+      }
+      qop[qb][w] = (int)c;
+      qlo[qb][w] = (int)lo;
+    }
+  }
+
+  // ---- tile schedule over the segments -------------------------------------
+  const int lo0 = (int)a.seg_lo[0], hi0 = (int)a.seg_hi[0];
+  const int lo1 = a.n_segments > 1 ? (int)a.seg_lo[1] : 0;
+  const int hi1 = a.n_segments > 1 ? (int)a.seg_hi[1] : 0;
+  const int t_first0 = (int)(lo0 / 64);
+  const int t_count0 = hi0 > lo0 ? (int)((hi0 - 1) / 64) - t_first0 + 1 : 0;
+  const int t_first1 = (int)(lo1 / 64);
+  const int t_count1 = hi1 > lo1 ? (int)((hi1 - 1) / 64) - t_first1 + 1 : 0;
+  const int n_all = t_count0 + t_count1;
+  const int pidx = part < 0 ? 0 : part % a.parts_per_unit;
+  const int pcount = part < 0 ? 1 : a.parts_per_unit;
+  const int it_begin = (int)((int64_t)n_all * pidx / pcount);
+  const int n_it = (int)((int64_t)n_all * (pidx + 1) / pcount) - it_begin;
+  auto tref = [&](int it) {
+    return tile_of(it_begin + it, t_count0, t_first0, t_first1, lo0, hi0, lo1, hi1);
+  };
+  auto clamp_it = [&](int it) { return it < n_it ? it : n_it - 1; };
+  auto stage_of = [&](int it) { return smem + (it & (kStages - 1)) * SM::STAGE; };
+
+  // Key rows of the lane's A operands: key16(kb, i) = row16 + 8 kb; factor
+  // records of the lane's keys key16(kb, 4 q4 + e) = frow + 8 kb + e.  (A
+  // quarter wave reads rows {8 kb + j} and {32 + 8 kb + j}, two to a bank
+  // group in the padded rows; swizzling the upper rows apart measured no
+  // faster.)
+  const int row16 = 32 * ((i16 >> 2) & 1) + 4 * (i16 >> 3) + (i16 & 3);
+  const int frow = 32 * (q4 & 1) + 4 * (q4 >> 1);
+  auto load_kop = [&](const uint8_t* st, v8i (&kop)[4]) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint8_t* krow = st + (row16 + 8 * kb) * SM::KROW + 32 * q4;
+      const uint4 k0 = *(const uint4*)(krow);
+      const uint4 k1 = *(const uint4*)(krow + 16);
+      kop[kb] = v8i{(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+    }
+  };
+  auto load_c = [&](const uint8_t* st, v4f (&cin)[4]) {
+    const float* cp = (const float*)(st + SM::KF_OFF) + 64 + frow;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float4 c4 = *(const float4*)(cp + 8 * kb);
+      cin[kb] = v4f{c4.x, c4.y, c4.z, c4.w};
+    }
+  };
+  // S = K . Q^T + C of key block kb for both query blocks
+  auto qk_step = [&](int kb, const v8i (&kop)[4], const v4f (&cin)[4], v4f (&acc)[4][2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      acc[kb][qb] = mfma16_fp8(kop[kb], qop[qb], cin[kb]);
+      if constexpr (QLO) acc[kb][qb] = mfma16_fp8_bscaled(kop[kb], qlo[qb], acc[kb][qb], 127 - kLoShift);
+    }
+  };
+  // keys of tile it outside its segment: add -448 * 448 to their raw scores
+  // (A: -448 at k = 0 of a masked key row, B: 448 at k = 0 of every query)
+  auto mask_scores = [&](int it, v4f (&acc)[4][2]) {
+    const TileRef tr = tref(it);
+    const int base = tr.tile * 64;
+    if (tr.lo > base || tr.hi < base + 64) {
+      const v8i ones = v8i{q4 == 0 ? 0x7E : 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int slot = base + row16 + 8 * kb;
+        const bool masked = !(slot >= tr.lo && slot < tr.hi);
+        const v8i bias = v8i{(q4 == 0 && masked) ? 0xFE : 0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) acc[kb][qb] = mfma16_fp8(bias, ones, acc[kb][qb]);
+      }
+    }
+  };
+  // O^T += V^T . P'^T and the row sum, as in attend_kernel
+  v16f acc_o[NDT];
+  v16f acc_l = v16f{};
+#pragma unroll
+  for (int d = 0; d < NDT; ++d) acc_o[d] = v16f{};
+  const int u_off = SM::U_OFF + (li < 2 ? li : 2) * SM::VROW + 32 * hh;
+  auto load_v = [&](const uint8_t* st, v8i (&vop)[NDT + 1]) {
+#pragma unroll
+    for (int d = 0; d <= NDT; ++d) {
+      const uint8_t* vrow = d < NDT ? st + SM::K_BYTES + (32 * d + li) * SM::VROW + 32 * hh : st + u_off;
+      const uint4 v0 = *(const uint4*)(vrow);
+      const uint4 v1 = *(const uint4*)(vrow + 16);
+      vop[d] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+    }
+  };
+  v8i pop = v8i{}, plo = v8i{};
+  auto pv_step = [&](int j, const v8i (&vop)[NDT + 1], int ev) {
+    if (j < NDT) {
+      acc_o[j] = mfma_fp8_scaled(vop[j], pop, acc_o[j], 127, ev);
+      if constexpr (PLO) acc_o[j] = mfma_fp8_scaled(vop[j], plo, acc_o[j], 127, ev - kLoShift);
+    } else {
+      acc_l = mfma_fp8_scaled(vop[NDT], pop, acc_l, 127 + 2, 127);
+      if constexpr (PLO) acc_l = mfma_fp8_scaled(vop[NDT], plo, acc_l, 127 + 2, 127 - kLoShift);
+    }
+  };
+  // P' of key block kb (chunk kb of the second half): codes of both query
+  // blocks, then the swap into the PV operand (dwords kb and 4 + kb)
+  auto probs_block = [&](int kb, const float (&t)[2][4][4]) {
+    uint32_t hi2[2], lo2[2] = {0u, 0u};
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if constexpr (PLO) {
+        float pp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pp[e] = __builtin_amdgcn_exp2f(t[qb][kb][e]);
+        uint32_t h = 0, l = 0;
+        split_fp8x2<false>(pp[0], pp[1], h, l);
+        split_fp8x2<true>(pp[2], pp[3], h, l);
+        hi2[qb] = h;
+        lo2[qb] = l;
+      } else {
+        uint32_t x = __builtin_amdgcn_cvt_pk_u8_f32(t[qb][kb][0], 0, __float_as_uint(t[qb][kb][0]));
+        x = __builtin_amdgcn_cvt_pk_u8_f32(t[qb][kb][1], 1, x);
+        x = __builtin_amdgcn_cvt_pk_u8_f32(t[qb][kb][2], 2, x);
+        x = __builtin_amdgcn_cvt_pk_u8_f32(t[qb][kb][3], 3, x);
+        hi2[qb] = x;
+      }
+    }
+    const auto s = __builtin_amdgcn_permlane16_swap(hi2[0], hi2[1], false, false);
+    pop[kb] = (int)s[0];
+    pop[4 + kb] = (int)s[1];
+    if constexpr (PLO) {
+      const auto sl = __builtin_amdgcn_permlane16_swap(lo2[0], lo2[1], false, false);
+      plo[kb] = (int)sl[0];
+      plo[4 + kb] = (int)sl[1];
+    }
+  };
+
+  // ---- prologue: as in attend_kernel ----------------------------------------
+  TileRegs regs;
+  if (n_it > 0) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      load_tile<D>(regs, tref(clamp_it(p)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
+      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale_u, inv_kscale, tid);
+    }
+    load_tile<D>(regs, tref(clamp_it(2)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
+  }
+  for (int i = tid; i < SM::V_BYTES / 16; i += kThreads)
+    ((uint4*)(stage_of(-1) + SM::K_BYTES))[i] = make_uint4(0, 0, 0, 0);
+  if (tid == 0) ((int*)(stage_of(-1) + SM::KF_OFF))[128] = 127;
+  if (tid < (kStages - 1) * (SM::VROW / 16))
+    ((uint4*)(smem + (tid / (SM::VROW / 16)) * SM::STAGE + SM::U_OFF + 2 * SM::VROW))[tid % (SM::VROW / 16)] =
+        make_uint4(0, 0, 0, 0);
+  __syncthreads();
+
+  v4f acc_s[4][2];
+  float m_run[2];
+  {
+    v8i kop[4];
+    v4f cin[4];
+    load_kop(stage_of(0), kop);
+    load_c(stage_of(0), cin);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qk_step(kb, kop, cin, acc_s);
+    if constexpr (MASK) mask_scores(0, acc_s);
+    const float* kf = (const float*)(stage_of(0) + SM::KF_OFF) + frow;
+    float t0[2][4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const float4 k4 = *(const float4*)(kf + 8 * kb);
+      const float kk[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t0[qb][kb][e] = acc_s[kb][qb][e] * kk[e];
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) m_run[qb] = quad_max(max16(t0[qb])) - LU::kReset;
+  }
+
+  auto tile_step = [&](const int it, const int r) __attribute__((always_inline)) {
+    // (0) staging of tile it + 2 and the loads of tile it + 3 (as in attend_kernel)
+    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(r + 2), kscale_u, inv_kscale, tid);
+    load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
+
+    // (1) the PV and row-sum products of tile it - 1, interleaved with the
+    // scores of tile it: t = fma(S, kf, -m), one key block (8 scores) per product
+    const float* kf = (const float*)(stage_of(r) + SM::KF_OFF) + frow;
+    float4 kf4[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) kf4[kb] = *(const float4*)(kf + 8 * kb);
+    v8i vop[NDT + 1];
+    load_v(stage_of(r + 3), vop);
+    const int ev = __builtin_amdgcn_readfirstlane(((const int*)(stage_of(r + 3) + SM::KF_OFF))[128]);
+    float t[2][4][4];
+#pragma unroll
+    for (int c = 0; c <= NDT; ++c) {
+      if (c < 4) {
+        const float kk[4] = {kf4[c].x, kf4[c].y, kf4[c].z, kf4[c].w};
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[qb][c][e] = __builtin_fmaf(acc_s[c][qb][e], kk[e], -m_run[qb]);
+      }
+      pv_step(c, vop, ev);
+      chunk_fence();
+    }
+    {
+      // lazy running max (rare): per query block, from the four lanes of each query
+      float mx = 0.0f;
+      {
+        float flat[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) flat[j] = t[j >> 4][(j >> 2) & 3][j & 3];
+        mx = max32(flat);
+      }
+      if (__builtin_expect(__any(mx > LU::kTop), 0)) {
+        float alpha[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float raw = quad_max(max16(t[qb])) + m_run[qb];
+          const float m_new = __builtin_fmaxf(m_run[qb], raw - LU::kReset);
+          const float shift = m_run[qb] - m_new;
+          alpha[qb] = exp2f(shift * (1.0f / LU::kUnit));
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[qb][kb][e] += shift;
+          m_run[qb] = m_new;
+        }
+        // the PV accumulators hold query 16 (q4 & 1) + i in lane (q4, i)
+        const float al = (q4 & 1) ? alpha[1] : alpha[0];
+#pragma unroll
+        for (int d = 0; d < NDT; ++d) acc_o[d] *= al;
+        acc_l *= al;
+      }
+    }
+
+    // (2) the score products of tile it + 1, interleaved with P' of tile it
+    {
+      v8i kop[4];
+      v4f cin[4];
+      load_kop(stage_of(r + 1), kop);
+      load_c(stage_of(r + 1), cin);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        probs_block(c, t);
+        qk_step(c, kop, cin, acc_s);
+        chunk_fence();
+      }
+      asm volatile("" ::"v"(pop));
+      if constexpr (PLO) asm volatile("" ::"v"(plo));
+      if constexpr (MASK) mask_scores(it + 1, acc_s);
+    }
+
+    __syncthreads();
+  };
+  for (int it0 = 0; it0 < n_it; it0 += kStages) {
+#pragma unroll
+    for (int r = 0; r < kStages; ++r)
+      if (it0 + r < n_it) tile_step(it0 + r, r);
+  }
+  {
+    v8i vop[NDT + 1];
+    load_v(stage_of(n_it - 1), vop);
+    const int ev = __builtin_amdgcn_readfirstlane(((const int*)(stage_of(n_it - 1) + SM::KF_OFF))[128]);
+#pragma unroll
+    for (int j = 0; j <= NDT; ++j) pv_step(j, vop, ev);
+  }
+
+  // ---- epilogue (PV layout: lane (hh, li) holds query li) -------------------
+  const float l_tot = xhalf_sum(acc_l[0] + acc_l[1]);
+  const int row = wrow + li;
+  const float m_q = (q4 & 1) ? m_run[1] : m_run[0];
+  if (part >= 0) {
+    const int q = wave * kQPW + li;
+    float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
+    const float inv_c = 1.0f / kPW;
+#pragma unroll
+    for (int d = 0; d < NDT; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * d + 8 * g + 4 * hh;
+        *(float4*)(po + d0) = make_float4(acc_o[d][4 * g + 0] * inv_c, acc_o[d][4 * g + 1] * inv_c,
+                                          acc_o[d][4 * g + 2] * inv_c, acc_o[d][4 * g + 3] * inv_c);
+      }
+    if (hh == 0)
+      *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) =
+          make_float2((m_q + LU::kOff) * (1.0f / LU::kUnit), l_tot / kPW);
+    return;
+  }
+  const float scale = 1.0f / l_tot;
+  if (row < a.n_tokens) {
+    uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D;
+#pragma unroll
+    for (int d = 0; d < NDT; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * d + 8 * g + 4 * hh;
+        uint2 w;
+        w.x = pack_bf16x2(acc_o[d][4 * g + 0] * scale, acc_o[d][4 * g + 1] * scale);
+        w.y = pack_bf16x2(acc_o[d][4 * g + 2] * scale, acc_o[d][4 * g + 3] * scale);
+        *(uint2*)(dst + d0) = w;
+      }
+  }
+}
+
 // Merge the key-range parts of the split units: for each query,
 // M = max_p m_p, w_p = 2^(m_p - M), O = sum_p w_p O_p / sum_p w_p l_p.
 // One workgroup = kCombineQ queries of one split unit (blockIdx.x: the unit,
@@ -977,7 +1446,7 @@ hipError_t attend_capacity(int* workgroups) {
   hipDeviceProp_t prop;
   if (e == hipSuccess) e = hipGetDeviceProperties(&prop, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_kernel<128, false, false, false>, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend16_kernel<false, false, false>, kThreads, 0);
   if (e != hipSuccess) return e;
   *workgroups = (per_cu > 0 ? per_cu : 1) * prop.multiProcessorCount;
   return hipSuccess;
@@ -1033,9 +1502,16 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
   } else {                                                \
     RTV_DISPATCH_MASK(DIM, false, false)                  \
   }
+  // head dim 128: attend16_kernel (16x16x128 score products); 64: attend_kernel
   if (head_dim == 128) {
+#undef RTV_LAUNCH
+#define RTV_LAUNCH(DIM, MASK, QL, PL) \
+  hipLaunchKernelGGL((attend16_kernel<MASK, QL, PL>), g, b, 0, stream, args)
     RTV_DISPATCH(128)
   } else {
+#undef RTV_LAUNCH
+#define RTV_LAUNCH(DIM, MASK, QL, PL) \
+  hipLaunchKernelGGL((attend_kernel<DIM, MASK, QL, PL>), g, b, 0, stream, args)
     RTV_DISPATCH(64)
   }
 #undef RTV_DISPATCH
