@@ -48,9 +48,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true",
                    help="time eagerly launched steps (default: replays of one captured HIP graph per step)")
-    p.add_argument("--workload", choices=["step", "projection"], default="step",
+    p.add_argument("--workload", choices=["step", "projection", "attention"], default="step",
                    help="projection: time the projection workload's chunk (per-tensor e4m3 of X, the FP8 "
-                        "QKV GEMM and the append) unfused and fused, one JSON line")
+                        "QKV GEMM and the append) unfused and fused, one JSON line; attention: one attention "
+                        "call at the stress ring's window lengths and at the GQA workload, one JSON line")
     p.add_argument("--no-growth", action="store_true",
                    help="fill the rings with appends only instead of timing the four window-growth steps "
                         "(the profiler runs use it, so that every attention dispatch sees the full window)")
@@ -310,8 +311,101 @@ def projection(args):
     print(json.dumps(result), flush=True)
 
 
+def attention_configs(args):
+    """One attention call at the two other configurations the hot path is
+    measured on:
+    - the stress ring: K/V Student-t (nu = 3) with 4 x20 outlier channels per
+      head and 1 % zero rows (the seeded host generator), two-term queries, a
+      24-frame ring read at every window length of its cycle, 4..24 frames;
+    - the projection workload's attention: 24 query heads over 12 KV heads
+      (GQA 2:1) at the full 32-frame ring, 95744 keys (inputs N(0,1) drawn on
+      the device).
+    Each call is timed between HIP events over `steps` calls after `warmup`."""
+    import torch
+
+    import kv_cache_attention_rtv_amd as rtv
+    from workloads import get_workload
+    from workloads.generate import device_normal_bf16, kv_student_t_outliers
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    def entry(wl, frames, ms):
+        keys = frames * wl.tokens_per_frame
+        tflops = 4.0 * wl.chunk_tokens * keys * wl.head_dim * wl.n_q_heads / (ms * 1e-3) / 1e12
+        return {"window_frames": frames, "keys": keys, "ms": round(ms, 4), "tflops": round(tflops, 1),
+                "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4)}
+
+    # the stress ring, filled with its own distribution
+    wl = get_workload("stress")
+    fills = wl.capacity_frames // wl.chunk_frames
+    cfg = rtv.RtvConfig(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame, wl.chunk_frames,
+                        wl.capacity_frames, (fills + 2) * wl.chunk_frames, wl.rope_base, query_terms=2)
+    cache = rtv.RtvCache(cfg, device=dev)
+    def bits_to_dev(bits):
+        return torch.from_numpy(bits.view("int16")).view(torch.bfloat16).to(dev)
+
+    for step in range(fills + 1):
+        k, v = kv_student_t_outliers(wl, 0, step, 0)
+        cache.append(0, bits_to_dev(k), bits_to_dev(v))
+        if step < fills:
+            cache.advance(0)
+    q = device_normal_bf16((wl.chunk_tokens, wl.n_q_heads, wl.head_dim), (5, 0, 0), dev)
+    out = torch.empty_like(q)
+    stress = []
+    for frames in wl.window_cycle:
+        ms = timed(lambda: cache.attend(0, q, out, max_window_frames=frames, stream=stream))
+        stress.append(entry(wl, frames, ms))
+    del cache, q, out
+
+    # the projection workload's GQA attention over the full ring
+    wp = get_workload("proj")
+    fills = wp.capacity_frames // wp.chunk_frames
+    cfg = rtv.RtvConfig(1, wp.n_q_heads, wp.n_kv_heads, wp.head_dim, wp.tokens_per_frame, wp.chunk_frames,
+                        wp.capacity_frames, (fills + 2) * wp.chunk_frames, wp.rope_base)
+    cache = rtv.RtvCache(cfg, device=dev)
+    kv_shape = (wp.chunk_tokens, wp.n_kv_heads, wp.head_dim)
+    for step in range(fills):
+        cache.append(0, device_normal_bf16(kv_shape, (6, step, 1), dev), device_normal_bf16(kv_shape, (6, step, 2), dev))
+        if step < fills - 1:
+            cache.advance(0)
+    q = device_normal_bf16((wp.chunk_tokens, wp.n_q_heads, wp.head_dim), (6, 0, 0), dev)
+    out = torch.empty_like(q)
+    gqa = entry(wp, wp.capacity_frames, timed(lambda: cache.attend(0, q, out, stream=stream)))
+    result = {
+        "metric": "ms per attention call at the stress ring (every window length) and the GQA workload",
+        "value": gqa["ms"], "unit": "ms", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+        "dtype": "fp8-e4m3 (f32 accumulate)", "data": "synthetic",
+        "config": {"workload": (f"stress: {wl.n_q_heads} heads x {wl.head_dim}, {wl.chunk_tokens}-token chunk, "
+                                f"Student-t K/V with outlier channels and zero rows, two-term queries, "
+                                f"{wl.capacity_frames}-frame ring, windows {list(wl.window_cycle)} frames; "
+                                f"gqa: {wp.n_q_heads} query heads over {wp.n_kv_heads} KV heads, "
+                                f"{wp.capacity_frames}-frame ring")},
+        "stress": stress, "gqa": gqa,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload == "attention":
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        attention_configs(args)
+        return
     if args.workload == "projection":
         if args.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)
