@@ -469,6 +469,103 @@ __device__ __forceinline__ void probs_quarter(int c, const float (&t)[32], v8i& 
 // work: LDS reads, scalar and global-read instructions may still move across
 __device__ __forceinline__ void chunk_fence() { __builtin_amdgcn_sched_barrier(0x0124); }
 
+// Work item of a workgroup: a whole unit (query tile x head; part = -1) or
+// one key-range part of a unit; false when the workgroup has none.
+__device__ __forceinline__ bool work_item(const AttendArgs& a, int& unit, int& part) {
+  const int xcd = blockIdx.x & 7;
+  const int local = blockIdx.x >> 3;
+  if (local < a.full_per_xcd) {
+    unit = xcd * a.full_per_xcd + local;
+    part = -1;
+    return unit < a.n_full;
+  }
+  const int j = xcd * a.parts_per_xcd + (local - a.full_per_xcd);
+  if (j >= a.n_parts) return false;
+  unit = a.n_full + j / a.parts_per_unit;
+  part = j;
+  return true;
+}
+
+// max |q| of the rotated query row `row` (clamped to the chunk) over the RoPE
+// pairs [P hh, P hh + P) of lane half hh, both halves of each pair
+template <int D>
+__device__ __forceinline__ float lane_q_amax(const AttendArgs& a, int row, int head, int hh) {
+  constexpr int P = D / 4;
+  const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
+  const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
+  const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < P; j += 8) {
+    const uint4 w0 = *(const uint4*)(q_src + P * hh + j);
+    const uint4 w1 = *(const uint4*)(q_src + D / 2 + P * hh + j);
+    const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
+    const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
+      const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
+      const float2 c = *(const float2*)(q_cs + 2 * (j + e));
+      const float r0 = x0 * c.x - x1 * c.y;
+      const float r1 = x1 * c.x + x0 * c.y;
+      m = __builtin_fmaxf(m, __builtin_fmaxf(fabsf(r0), fabsf(r1)));
+    }
+  }
+  return m;
+}
+
+// The workgroup's max of x (one barrier; red holds one value per wave)
+__device__ __forceinline__ float wg_max(float x, float* red, int wave, int lane) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, o));
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  x = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) x = __builtin_fmaxf(x, red[w]);
+  return x;
+}
+
+// Result of one lane for its query (PV layout: lane (hh, li) holds query li
+// of a 32-query sub-tile, q its index in the workgroup): a whole unit writes O
+// = acc / L as bf16; a key-range part writes sum p V / 55 and (m, sum p / 55)
+// with m back in log2 units (u = kUnit t + kOff, so m = (m_u + kOff) / kUnit).
+template <int D, class LU>
+__device__ __forceinline__ void write_result(const AttendArgs& a, const v16f (&o)[D / 32], float l_tot, float m_u,
+                                             int part, int q, int row, int head, int hh) {
+  constexpr int NDT = D / 32;
+  if (part >= 0) {
+    float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
+    const float inv_c = 1.0f / kPW;
+#pragma unroll
+    for (int d = 0; d < NDT; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * d + 8 * g + 4 * hh;
+        *(float4*)(po + d0) = make_float4(o[d][4 * g + 0] * inv_c, o[d][4 * g + 1] * inv_c,
+                                          o[d][4 * g + 2] * inv_c, o[d][4 * g + 3] * inv_c);
+      }
+    if (hh == 0)
+      *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) =
+          make_float2((m_u + LU::kOff) * (1.0f / LU::kUnit), l_tot / kPW);
+    return;
+  }
+  const float scale = 1.0f / l_tot;
+  if (row < a.n_tokens) {
+    uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D;
+#pragma unroll
+    for (int d = 0; d < NDT; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * d + 8 * g + 4 * hh;
+        uint2 w;
+        w.x = pack_bf16x2(o[d][4 * g + 0] * scale, o[d][4 * g + 1] * scale);
+        w.y = pack_bf16x2(o[d][4 * g + 2] * scale, o[d][4 * g + 3] * scale);
+        *(uint2*)(dst + d0) = w;
+      }
+  }
+}
+
 // MASK = false: every segment boundary of the window falls on a 64-slot tile
 // boundary (the host checks), so no tile needs masking and the kernel carries
 // no masking code.  MASK = true handles any boundary.
@@ -491,20 +588,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * SM::STAGE];
   __shared__ float red[kWaves];
 
-  // work item: a whole unit (query tile x head) or one key-range part of one
-  const int xcd = blockIdx.x & 7;
-  const int local = blockIdx.x >> 3;
   int unit, part;
-  if (local < a.full_per_xcd) {
-    unit = xcd * a.full_per_xcd + local;
-    if (unit >= a.n_full) return;
-    part = -1;
-  } else {
-    const int j = xcd * a.parts_per_xcd + (local - a.full_per_xcd);
-    if (j >= a.n_parts) return;
-    unit = a.n_full + j / a.parts_per_unit;
-    part = j;
-  }
+  if (!work_item(a, unit, part)) return;
   const int head = unit / a.n_qtiles;
   const int qtile = unit % a.n_qtiles;
   const int kvh = head / a.group;
@@ -528,35 +613,10 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   float qamax = 0.0f;
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub) {
-    const int row = qtile * kQPB + wave * kQPW + sub * 32 + li;
-    q_rows[sub] = row;
-    const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
-    const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
-    const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
-#pragma unroll
-    for (int j = 0; j < P; j += 8) {
-      const uint4 w0 = *(const uint4*)(q_src + P * hh + j);
-      const uint4 w1 = *(const uint4*)(q_src + D / 2 + P * hh + j);
-      const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
-      const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
-        const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
-        const float2 c = *(const float2*)(q_cs + 2 * (j + e));
-        const float r0 = x0 * c.x - x1 * c.y;
-        const float r1 = x1 * c.x + x0 * c.y;
-        qamax = __builtin_fmaxf(qamax, __builtin_fmaxf(fabsf(r0), fabsf(r1)));
-      }
-    }
+    q_rows[sub] = qtile * kQPB + wave * kQPW + sub * 32 + li;
+    qamax = __builtin_fmaxf(qamax, lane_q_amax<D>(a, q_rows[sub], head, hh));
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) qamax = __builtin_fmaxf(qamax, __shfl_xor(qamax, o));
-  if (lane == 0) red[wave] = qamax;
-  __syncthreads();
-  qamax = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) qamax = __builtin_fmaxf(qamax, red[w]);
+  qamax = wg_max(qamax, red, wave, lane);
   const float q_inv = qamax > 0.0f ? kFp8Max / qamax : 0.0f;
   const float kscale = __builtin_fmaxf((qamax / kFp8Max) * (kLog2e / sqrtf((float)D)), kScaleMin);
   const float inv_kscale = 1.0f / kscale;
@@ -859,47 +919,13 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     // row sum: rows 0 and 1 of L (registers 0 and 1 of the lanes hh = 0; the
     // same registers of the lanes hh = 1 hold the zero rows 4 and 5)
     const float l_tot = xhalf_sum(acc_l[sub][0] + acc_l[sub][1]);
-    const int row = q_rows[sub];
-    if (part >= 0) {
-      // partial result of a key range: sum p V and sum p (p = 2^(score - m)),
-      // with m
-      const int q = wave * kQPW + sub * 32 + li;
-      float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
-      const float inv_c = 1.0f / kPW;
-#pragma unroll
-      for (int d = 0; d < NDT; ++d)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * d + 8 * g + 4 * hh;
-          *(float4*)(po + d0) = make_float4(acc_o[sub][d][4 * g + 0] * inv_c, acc_o[sub][d][4 * g + 1] * inv_c,
-                                            acc_o[sub][d][4 * g + 2] * inv_c, acc_o[sub][d][4 * g + 3] * inv_c);
-        }
-      // (m back in log2 units: u = kUnit t + kOff with m_u = kUnit m - kOff)
-      if (hh == 0)
-        *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) =
-            make_float2((m_run[sub] + LU::kOff) * (1.0f / LU::kUnit), l_tot / kPW);
-      continue;
-    }
-    const float scale = 1.0f / l_tot;
-    if (row < a.n_tokens) {
-      uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D;
-#pragma unroll
-      for (int d = 0; d < NDT; ++d)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * d + 8 * g + 4 * hh;
-          uint2 w;
-          w.x = pack_bf16x2(acc_o[sub][d][4 * g + 0] * scale, acc_o[sub][d][4 * g + 1] * scale);
-          w.y = pack_bf16x2(acc_o[sub][d][4 * g + 2] * scale, acc_o[sub][d][4 * g + 3] * scale);
-          *(uint2*)(dst + d0) = w;
-        }
-    }
+    write_result<D, LU>(a, acc_o[sub], l_tot, m_run[sub], part, wave * kQPW + sub * 32 + li, q_rows[sub], head, hh);
   }
 }
 
 // ---- head dim 128: scores by v_mfma_f32_16x16x128_f8f6f4 -------------------
-// The same computation as attend_kernel<128, ...> with the score products taken
-// 16 keys x 16 queries at a time over the whole head dimension.  Lane (q4 =
+// The computation of attend_kernel (which serves head dim 64), with the score
+// products taken 16 keys x 16 queries at a time over the whole head dimension.  Lane (q4 =
 // lane / 16, i = lane % 16) then holds, for each of the tile's four 16-key
 // blocks kb and the wave's two 16-query blocks qb, the scores of keys
 // key16(kb, 4 q4 + e) (e = 0..3) for query 16 qb + i: 16 keys x 2 queries,
@@ -951,20 +977,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * SM::STAGE];
   __shared__ float red[kWaves];
 
-  // work item: a whole unit (query tile x head) or one key-range part of one
-  const int xcd = blockIdx.x & 7;
-  const int local = blockIdx.x >> 3;
   int unit, part;
-  if (local < a.full_per_xcd) {
-    unit = xcd * a.full_per_xcd + local;
-    if (unit >= a.n_full) return;
-    part = -1;
-  } else {
-    const int j = xcd * a.parts_per_xcd + (local - a.full_per_xcd);
-    if (j >= a.n_parts) return;
-    unit = a.n_full + j / a.parts_per_unit;
-    part = j;
-  }
+  if (!work_item(a, unit, part)) return;
   const int head = unit / a.n_qtiles;
   const int qtile = unit % a.n_qtiles;
   const int kvh = head / a.group;
@@ -987,36 +1001,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
 
   // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
   const int wrow = qtile * kQPB + wave * kQPW;  // first query row of the wave
-  float qamax = 0.0f;
-  {
-    const int row = wrow + li;
-    const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
-    const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
-    const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
-#pragma unroll
-    for (int j = 0; j < P; j += 8) {
-      const uint4 w0 = *(const uint4*)(q_src + P * hh + j);
-      const uint4 w1 = *(const uint4*)(q_src + D / 2 + P * hh + j);
-      const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
-      const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
-        const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
-        const float2 c = *(const float2*)(q_cs + 2 * (j + e));
-        const float r0 = x0 * c.x - x1 * c.y;
-        const float r1 = x1 * c.x + x0 * c.y;
-        qamax = __builtin_fmaxf(qamax, __builtin_fmaxf(fabsf(r0), fabsf(r1)));
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) qamax = __builtin_fmaxf(qamax, __shfl_xor(qamax, o));
-  if (lane == 0) red[wave] = qamax;
-  __syncthreads();
-  qamax = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) qamax = __builtin_fmaxf(qamax, red[w]);
+  const float qamax = wg_max(lane_q_amax<D>(a, wrow + li, head, hh), red, wave, lane);
   const float q_inv = qamax > 0.0f ? kFp8Max / qamax : 0.0f;
   const float kscale = __builtin_fmaxf((qamax / kFp8Max) * (kLog2e / sqrtf((float)D)), kScaleMin);
   const float inv_kscale = 1.0f / kscale;
@@ -1090,8 +1075,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
   // quarter wave reads rows {8 kb + j} and {32 + 8 kb + j}, two to a bank
   // group in the padded rows; swizzling the upper rows apart measured no
   // faster.)
-  const int row16 = 32 * ((i16 >> 2) & 1) + 4 * (i16 >> 3) + (i16 & 3);
-  const int frow = 32 * (q4 & 1) + 4 * (q4 >> 1);
+  const int row16 = key16(0, i16);          // = 32 ((i16 >> 2) & 1) + 4 (i16 >> 3) + (i16 & 3)
+  const int frow = key16(0, 4 * q4);        // = 32 (q4 & 1) + 4 (q4 >> 1)
   auto load_kop = [&](const uint8_t* st, v8i (&kop)[4]) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -1325,41 +1310,9 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
     for (int j = 0; j <= NDT; ++j) pv_step(j, vop, ev);
   }
 
-  // ---- epilogue (PV layout: lane (hh, li) holds query li) -------------------
+  // ---- epilogue (PV layout: lane (hh, li) holds query li, the query block q4 & 1)
   const float l_tot = xhalf_sum(acc_l[0] + acc_l[1]);
-  const int row = wrow + li;
-  const float m_q = (q4 & 1) ? m_run[1] : m_run[0];
-  if (part >= 0) {
-    const int q = wave * kQPW + li;
-    float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
-    const float inv_c = 1.0f / kPW;
-#pragma unroll
-    for (int d = 0; d < NDT; ++d)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * d + 8 * g + 4 * hh;
-        *(float4*)(po + d0) = make_float4(acc_o[d][4 * g + 0] * inv_c, acc_o[d][4 * g + 1] * inv_c,
-                                          acc_o[d][4 * g + 2] * inv_c, acc_o[d][4 * g + 3] * inv_c);
-      }
-    if (hh == 0)
-      *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) =
-          make_float2((m_q + LU::kOff) * (1.0f / LU::kUnit), l_tot / kPW);
-    return;
-  }
-  const float scale = 1.0f / l_tot;
-  if (row < a.n_tokens) {
-    uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D;
-#pragma unroll
-    for (int d = 0; d < NDT; ++d)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * d + 8 * g + 4 * hh;
-        uint2 w;
-        w.x = pack_bf16x2(acc_o[d][4 * g + 0] * scale, acc_o[d][4 * g + 1] * scale);
-        w.y = pack_bf16x2(acc_o[d][4 * g + 2] * scale, acc_o[d][4 * g + 3] * scale);
-        *(uint2*)(dst + d0) = w;
-      }
-  }
+  write_result<D, LU>(a, acc_o, l_tot, (q4 & 1) ? m_run[1] : m_run[0], part, wave * kQPW + li, wrow + li, head, hh);
 }
 
 // Merge the key-range parts of the split units: for each query,
