@@ -69,6 +69,16 @@ typedef struct rtv_config {
                               * 20% more attention time on long windows).  Windows shorter
                               * than 8192 keys always use two terms for queries and
                               * probabilities. */
+  int32_t prob_terms;        /* e4m3 terms carrying each attention weight P' into the PV
+                              * product on windows of 8192 keys or more:
+                              * 1 (or 0): one code read off the log domain, within one code
+                              * step of the correctly rounded value (up to about 6% per
+                              * weight), which averages out when the weight spreads over
+                              * many keys;
+                              * 2: exp2 and two terms (relative error about 2^-8), with the
+                              * queries also in two terms, for peaked attention where a
+                              * few keys carry most of the weight (the configuration of
+                              * windows under 8192 keys, on every window). */
   double rope_base;          /* RoPE base (10000) */
 } rtv_config;
 

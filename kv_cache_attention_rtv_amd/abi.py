@@ -39,6 +39,7 @@ class rtv_config(ctypes.Structure):
         ("capacity_frames", ctypes.c_int32),
         ("max_global_frames", ctypes.c_int32),
         ("query_terms", ctypes.c_int32),
+        ("prob_terms", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
     ]
 

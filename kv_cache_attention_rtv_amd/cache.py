@@ -25,11 +25,13 @@ class RtvConfig:
     max_global_frames: int
     rope_base: float = 10000.0
     query_terms: int = 1        # 2: two-term e4m3 queries (keys with outlier channels)
+    prob_terms: int = 1         # 2: two-term attention weights on long windows (peaked attention)
 
     def to_c(self) -> abi.rtv_config:
         return abi.rtv_config(self.n_layers, self.n_q_heads, self.n_kv_heads, self.head_dim,
                               self.tokens_per_frame, self.chunk_frames, self.capacity_frames,
-                              self.max_global_frames, int(self.query_terms), float(self.rope_base))
+                              self.max_global_frames, int(self.query_terms), int(self.prob_terms),
+                              float(self.rope_base))
 
     @property
     def chunk_tokens(self) -> int:

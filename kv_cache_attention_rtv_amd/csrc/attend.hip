@@ -1416,7 +1416,7 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
       keys += args.seg_hi[s] - args.seg_lo[s];
     }
     n_tiles = attend_window_tiles(args);
-    short_window = keys < kPreciseKeys;
+    short_window = keys < kPreciseKeys || args.two_term_p;
     attend_schedule(args, n_tiles, kMaxParts);
     grid_per_xcd = args.full_per_xcd + args.parts_per_xcd;
     rem = args.n_work - args.n_full;
@@ -1428,7 +1428,7 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
     const RingShape& sh = args.shape;
     const int64_t chunk = (int64_t)sh.chunk_frames * sh.tokens_per_frame;
     aligned = chunk % 64 == 0 && sh.max_window_frames % sh.chunk_frames == 0;
-    short_window = chunk < kPreciseKeys;
+    short_window = chunk < kPreciseKeys || args.two_term_p;
     n_tiles = (int)(((int64_t)sh.capacity_frames * sh.tokens_per_frame + 63) / 64) + 1;
     AttendArgs whole = args, most = args;
     attend_schedule(whole, 1, kMaxParts);

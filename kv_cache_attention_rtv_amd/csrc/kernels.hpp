@@ -70,6 +70,7 @@ struct AttendArgs {
   int32_t n_work;         // n_qtiles * n_q_heads (units of work)
   int32_t capacity;       // workgroups the device runs concurrently (0 = never split)
   int32_t two_term_q;     // queries as two e4m3 terms on every window
+  int32_t two_term_p;     // P' (and queries) as two e4m3 terms on every window
   // schedule (filled by launch_attend): units [0, n_full) run whole windows; units [n_full, n_work) are
   // split into parts_per_unit key ranges whose partial (O, m, l) go to the
   // workspace and are merged by the combine kernel

@@ -65,6 +65,7 @@ rtv_status check_config(const rtv_config* c) {
   if (c->max_global_frames < c->chunk_frames) return RTV_ERR_INVALID_ARG;
   if (!(c->rope_base > 0.0) || !std::isfinite(c->rope_base)) return RTV_ERR_INVALID_ARG;
   if (c->query_terms < 0 || c->query_terms > 2) return RTV_ERR_INVALID_ARG;
+  if (c->prob_terms < 0 || c->prob_terms > 2) return RTV_ERR_INVALID_ARG;
   int64_t chunk;
   if (!mul_ok(c->chunk_frames, c->tokens_per_frame, &chunk) || chunk > INT32_MAX) return RTV_ERR_INVALID_ARG;
   return RTV_OK;
@@ -398,6 +399,7 @@ rtv_status rtv_attend(rtv_cache* c, int32_t layer, const void* q_bf16, int64_t q
   a.n_work = a.n_qtiles * cfg.n_q_heads;
   a.capacity = c->capacity;
   a.two_term_q = cfg.query_terms == 2;
+  a.two_term_p = cfg.prob_terms == 2;
   rtv::attend_set_workspace(a, c->ws, cfg.head_dim, cfg.n_kv_heads, c->plan.slots_padded);
   if (rtv::launch_attend(a, cfg.head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
     return RTV_ERR_HIP;

@@ -22,14 +22,14 @@ MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
 
 
-def _caches(rtv, wl, max_global_frames=None, n_layers=None, query_terms=1):
+def _caches(rtv, wl, max_global_frames=None, n_layers=None, query_terms=1, prob_terms=1):
     steps = max(wl.steps, 1)
     cfg = rtv.RtvConfig(
         n_layers=n_layers or wl.n_layers, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
         head_dim=wl.head_dim, tokens_per_frame=wl.tokens_per_frame, chunk_frames=wl.chunk_frames,
         capacity_frames=wl.capacity_frames,
         max_global_frames=max_global_frames or (steps + 2) * wl.chunk_frames,
-        rope_base=wl.rope_base, query_terms=query_terms)
+        rope_base=wl.rope_base, query_terms=query_terms, prob_terms=prob_terms)
     gpu = rtv.RtvCache(cfg)
     ora = OracleKVCache(cfg.n_layers, wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame,
                         wl.chunk_frames, wl.capacity_frames, wl.rope_base)
@@ -320,3 +320,82 @@ def test_append_extreme_row_magnitudes(rtv_lib, D, H):
             assert bad.size == 0, (what, step, bad[:4].tolist(), [int(cls[t, h]) for t, h, *_ in bad[:4]])
         gpu.advance(0)
         ora.advance(0)
+
+
+@pytest.mark.parametrize("T", [1024, 96])
+def test_attention_rescales_when_later_keys_score_higher(rtv_lib, T):
+    """Two chunks whose first 64 keys (the window's first tile) have K scaled
+    by 1/4 (exact in bf16): the running max starts from that tile and then has
+    to move for most queries during the walk, at different tiles for different
+    queries (both query blocks of a lane, the 4-lane reduction and the
+    per-lane factor of the rescale), while the softmax over the whole window
+    keeps the shape of the N(0,1) workloads.  T = 1024: 8192-key window (codes
+    of P' from the log domain); T = 96: 768 keys (two-term P').  12 heads of
+    128 over 6 KV heads (GQA 2:1); attention on sampled rows."""
+    from oracle import quant
+    from workloads.generate import bf16_bits_to_f32, f32_to_bf16_bits
+    wl = dataclasses.replace(get_workload("tiny"), grid_h=1, grid_w=T, chunk_frames=4, capacity_frames=8,
+                             head_dim=128, n_kv_heads=6, n_q_heads=12)
+    gpu, ora = _caches(rtv_lib, wl, max_global_frames=4 * wl.chunk_frames)
+    n = wl.chunk_tokens
+    rows = np.unique(np.concatenate([[0, 31, 32, 255, 256, n - 1], np.random.default_rng(9).integers(0, n, 26)]))
+    for step in range(2):
+        q, k, v = qkv_normal(wl, 0, step, 0)
+        if step == 0:
+            kf = bf16_bits_to_f32(k).reshape(k.shape)
+            kf[:64] *= np.float32(0.25)
+            k = f32_to_bf16_bits(kf).reshape(k.shape)
+        print(f"rescale T={T} step={step}", flush=True)
+        gpu.append(0, to_dev_bf16(k), to_dev_bf16(v))
+        ora.append(0, k, v)
+        if step == 0:
+            gpu.advance(0)
+            ora.advance(0)
+    # the max does move: for most sampled rows the window's top score is more
+    # than 3 octaves above the top score of its first 64 keys (the headroom the
+    # running max leaves)
+    q_rot = ora.rotated_queries(0, q)
+    _, _, kc, ks, _, _ = ora.window(0)
+    kd = quant.dequantize_rows(kc[:, 0, :], ks[:, 0])
+    s = (q_rot[rows, 0, :].astype(np.float64) @ kd.T) / np.sqrt(128.0) * np.log2(np.e)
+    rising = np.mean(s.max(axis=1) - s[:, :64].max(axis=1) > 3.0)
+    print(f"rows whose max rises > 3 octaves after the first tile: {rising:.2f}", flush=True)
+    assert rising >= 0.5
+    out = gpu.attend(0, to_dev_bf16(q))
+    want = ora.attend(0, q, rows=rows)
+    mx, mean = attention_errors(bf16_to_np_f32(out)[rows], want)
+    print(f"rescale T={T} attention max={mx:.3e} mean={mean:.3e}", flush=True)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS
+
+
+@pytest.mark.parametrize("prob_terms", [1, 2])
+def test_peaked_attention_and_two_term_weights(rtv_lib, prob_terms):
+    """Peaked attention on an 8192-key window: the second chunk's K doubled
+    (exact in bf16), so its scores spread twice as wide and a few keys carry
+    much of each row's weight.  The one-code weights of long windows (within
+    one code step of the rounded value) then no longer average out: their
+    error is reported, and the cache created with prob_terms = 2 (exp2 and two
+    e4m3 terms per weight) must meet the tolerance.  12 heads of 128 over 6 KV
+    heads; attention on sampled rows."""
+    from workloads.generate import bf16_bits_to_f32, f32_to_bf16_bits
+    wl = dataclasses.replace(get_workload("tiny"), grid_h=1, grid_w=1024, chunk_frames=4, capacity_frames=8,
+                             head_dim=128, n_kv_heads=6, n_q_heads=12)
+    gpu, ora = _caches(rtv_lib, wl, max_global_frames=4 * wl.chunk_frames, prob_terms=prob_terms)
+    n = wl.chunk_tokens
+    rows = np.unique(np.concatenate([[0, 31, 32, 255, 256, n - 1], np.random.default_rng(9).integers(0, n, 26)]))
+    for step in range(2):
+        q, k, v = qkv_normal(wl, 0, step, 0)
+        if step == 1:
+            k = f32_to_bf16_bits(bf16_bits_to_f32(k) * np.float32(2.0)).reshape(k.shape)
+        print(f"peaked prob_terms={prob_terms} step={step}", flush=True)
+        gpu.append(0, to_dev_bf16(k), to_dev_bf16(v))
+        ora.append(0, k, v)
+        if step == 0:
+            gpu.advance(0)
+            ora.advance(0)
+    out = gpu.attend(0, to_dev_bf16(q))
+    want = ora.attend(0, q, rows=rows)
+    mx, mean = attention_errors(bf16_to_np_f32(out)[rows], want)
+    print(f"peaked prob_terms={prob_terms} attention max={mx:.3e} mean={mean:.3e}", flush=True)
+    if prob_terms == 2:
+        assert mx <= MAX_ABS and mean <= MEAN_ABS

@@ -89,6 +89,8 @@ def test_cache_bytes_and_config_validation():
         rtv.RtvConfig(1, 12, 12, 128, 0, 4, 16, 64),
         rtv.RtvConfig(1, 12, 12, 128, 2992, 4, 16, 64, query_terms=3),
         rtv.RtvConfig(1, 12, 12, 128, 2992, 4, 16, 64, query_terms=-1),
+        rtv.RtvConfig(1, 12, 12, 128, 2992, 4, 16, 64, prob_terms=3),
+        rtv.RtvConfig(1, 12, 12, 128, 2992, 4, 16, 64, prob_terms=-1),
     ]
     for c in bad:
         with pytest.raises(rtv.RtvError) as e:
