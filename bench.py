@@ -384,6 +384,28 @@ def attention_configs(args):
     q = device_normal_bf16((wp.chunk_tokens, wp.n_q_heads, wp.head_dim), (6, 0, 0), dev)
     out = torch.empty_like(q)
     gqa = entry(wp, wp.capacity_frames, timed(lambda: cache.attend(0, q, out, stream=stream)))
+    del cache, q, out
+
+    # the step's layer shape at the full window, with one-code (default) and
+    # two-term attention weights (prob_terms = 2, the choice for peaked rows)
+    ws = get_workload("step")
+    fills = ws.capacity_frames // ws.chunk_frames
+    kv_shape = (ws.chunk_tokens, ws.n_kv_heads, ws.head_dim)
+    weights = {}
+    for terms in (1, 2):
+        cfg = rtv.RtvConfig(1, ws.n_q_heads, ws.n_kv_heads, ws.head_dim, ws.tokens_per_frame, ws.chunk_frames,
+                            ws.capacity_frames, (fills + 2) * ws.chunk_frames, ws.rope_base, prob_terms=terms)
+        cache = rtv.RtvCache(cfg, device=dev)
+        for step in range(fills):
+            cache.append(0, device_normal_bf16(kv_shape, (7, step, 1), dev),
+                         device_normal_bf16(kv_shape, (7, step, 2), dev))
+            if step < fills - 1:
+                cache.advance(0)
+        q = device_normal_bf16((ws.chunk_tokens, ws.n_q_heads, ws.head_dim), (7, 0, 0), dev)
+        out = torch.empty_like(q)
+        weights[f"prob_terms_{terms}"] = entry(ws, ws.capacity_frames,
+                                               timed(lambda: cache.attend(0, q, out, stream=stream)))
+        del cache, q, out
     result = {
         "metric": "ms per attention call at the stress ring (every window length) and the GQA workload",
         "value": gqa["ms"], "unit": "ms", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
@@ -392,8 +414,9 @@ def attention_configs(args):
                                 f"Student-t K/V with outlier channels and zero rows, two-term queries, "
                                 f"{wl.capacity_frames}-frame ring, windows {list(wl.window_cycle)} frames; "
                                 f"gqa: {wp.n_q_heads} query heads over {wp.n_kv_heads} KV heads, "
-                                f"{wp.capacity_frames}-frame ring")},
-        "stress": stress, "gqa": gqa,
+                                f"{wp.capacity_frames}-frame ring; layer: the step's layer shape at "
+                                f"{ws.capacity_frames} frames, prob_terms 1 and 2")},
+        "stress": stress, "gqa": gqa, "layer_full_window": weights,
     }
     print(json.dumps(result), flush=True)
 
