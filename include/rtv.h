@@ -78,7 +78,8 @@ typedef struct rtv_config {
                               * 2: exp2 and two terms (relative error about 2^-8), with the
                               * queries also in two terms, for peaked attention where a
                               * few keys carry most of the weight (the configuration of
-                              * windows under 8192 keys, on every window). */
+                              * windows under 8192 keys, on every window; about 1.9 times
+                              * the attention time on a 47872-key window). */
   double rope_base;          /* RoPE base (10000) */
 } rtv_config;
 
