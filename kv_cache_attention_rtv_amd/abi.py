@@ -8,6 +8,11 @@ is missing, and there is no fallback implementation.
 from __future__ import annotations
 
 import ctypes
+
+# torch's HIP runtime is loaded before the library, so the library binds to
+# the runtime that owns the tensors it is handed (a second runtime loaded
+# first would see torch's device pointers as invalid)
+import torch  # noqa: F401
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
