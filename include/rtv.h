@@ -71,16 +71,35 @@ typedef struct rtv_config {
                               * probabilities. */
   int32_t prob_terms;        /* e4m3 terms carrying each attention weight P' into the PV
                               * product on windows of 8192 keys or more:
-                              * 1 (or 0): one code read off the log domain, within one code
-                              * step of the correctly rounded value (up to about 6% per
-                              * weight), which averages out when the weight spreads over
-                              * many keys;
-                              * 2: exp2 and two terms (relative error about 2^-8), with the
-                              * queries also in two terms, for peaked attention where a
-                              * few keys carry most of the weight (the configuration of
-                              * windows under 8192 keys, on every window; about 1.9 times
-                              * the attention time on a 47872-key window). */
+                              * 0 (default): one code read off the log domain (within one
+                              * code step of the correctly rounded value, up to about 6%
+                              * per weight), checked: every query row also measures how
+                              * few keys carry its weight (sum of squared weights, on the
+                              * matrix cores), and the query tiles holding a row above
+                              * 5e-4 are recomputed in a second launch with queries and
+                              * weights as two e4m3 terms (relative error about 2^-8).
+                              * Rows whose weight spreads over many keys, where the
+                              * one-code errors average out, cost one extra matrix-core
+                              * product per tile; each recomputed query tile costs about
+                              * twice its one-code time;
+                              * 1: one code, unchecked: outside the attention tolerance on
+                              * peaked rows (a few keys carrying much of the weight);
+                              * 2: two terms on every window, for callers that know their
+                              * attention is peaked (the configuration of windows under
+                              * 8192 keys, which always take it; about 1.9 times the
+                              * one-code time on a 47872-key window). */
   double rope_base;          /* RoPE base (10000) */
+  const float* rope_cos_sin_host;
+                             /* optional host table [max_global_frames*T][D/2][2] of the
+                              * (cos, sin) pairs of every position, read once by
+                              * rtv_cache_create (the caller keeps ownership); NULL: the
+                              * library computes it as rtv_rope_fill_host does.  Callers
+                              * that check the codes against another implementation pass
+                              * one table to both, so that no libm difference can move a
+                              * code.  The arena holds the table for the whole session:
+                              * max_global_frames * T * D * 4 bytes (1.53 MB per frame of
+                              * 2992 tokens at D = 128; 132 GB for an hour at 24 frames
+                              * per second), so max_global_frames bounds a session. */
 } rtv_config;
 
 /* Device layout of one layer's ring, for read-back and for callers that fuse
@@ -217,6 +236,13 @@ rtv_status rtv_device_state_end(rtv_cache* cache, void* stream);
 /* ---- inspection (tests, fused producers) -------------------------------- */
 
 rtv_status rtv_cache_layout(const rtv_cache* cache, int32_t layer, rtv_layout* out);
+
+/* Number of query tiles (units of 256 queries of one query head) that the
+ * latest rtv_attend on this cache flagged as peaked and recomputed with
+ * two-term queries and weights (prob_terms 0; 0 for calls that took another
+ * variant).  Copies one word from the arena and synchronizes `stream`: for
+ * tests and monitoring, not the hot path. */
+rtv_status rtv_cache_peaked_units(const rtv_cache* cache, int32_t* units, void* stream);
 
 /* The window an attend of `layer` would read now. */
 rtv_status rtv_cache_window(const rtv_cache* cache, int32_t layer,

@@ -1,8 +1,8 @@
 """ctypes binding of librtv.so: the C ABI of include/rtv.h under the same names.
 
 Argument marshalling only: every step of the path runs in the library's HIP
-kernels.  The library must have been built (``python -m
-kv_cache_attention_rtv_amd.build``); importing this module fails loudly if it
+kernels.  The library must have been built (``python
+kv_cache_attention_rtv_amd/build.py``); importing this module fails loudly if it
 is missing, and there is no fallback implementation.
 """
 from __future__ import annotations
@@ -46,6 +46,7 @@ class rtv_config(ctypes.Structure):
         ("query_terms", ctypes.c_int32),
         ("prob_terms", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
+        ("rope_cos_sin_host", ctypes.c_void_p),
     ]
 
 
@@ -78,7 +79,7 @@ class rtv_window(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m kv_cache_attention_rtv_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python kv_cache_attention_rtv_amd/build.py` "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -93,6 +94,7 @@ def _load():
         "rtv_device_state_end": (I32, [P, P]),
         "rtv_cache_layout": (I32, [P, I32, ctypes.POINTER(rtv_layout)]),
         "rtv_cache_window": (I32, [P, I32, I32, ctypes.POINTER(rtv_window)]),
+        "rtv_cache_peaked_units": (I32, [P, ctypes.POINTER(I32), P]),
         "rtv_ring_window": (I32, [I64, I32, I32, I32, I32, I32, ctypes.POINTER(rtv_window)]),
         "rtv_rope_fill_host": (I32, [I32, ctypes.c_double, I64, I64, P]),
         "rtv_encode_e4m3": (I32, [P, P, I64, P]),
@@ -118,7 +120,8 @@ def _load():
 lib = _load()
 EXPORTED = (
     "rtv_cache_bytes", "rtv_cache_create", "rtv_destroy", "rtv_append_rope_quant",
-    "rtv_attend", "rtv_advance", "rtv_device_state_begin", "rtv_device_state_end", "rtv_cache_layout", "rtv_cache_window", "rtv_ring_window",
+    "rtv_attend", "rtv_advance", "rtv_device_state_begin", "rtv_device_state_end", "rtv_cache_layout",
+    "rtv_cache_window", "rtv_cache_peaked_units", "rtv_ring_window",
     "rtv_rope_fill_host", "rtv_encode_e4m3", "rtv_status_string",
     "rtv_quant_workspace_bytes", "rtv_quant_fp8_per_tensor", "rtv_gemm_fp8", "rtv_qkv_gemm_append",
 )
@@ -183,6 +186,12 @@ def rtv_cache_window(handle, layer, max_window_frames=0) -> rtv_window:
     out = rtv_window()
     check(lib.rtv_cache_window(handle, layer, max_window_frames, ctypes.byref(out)), "rtv_cache_window")
     return out
+
+
+def rtv_cache_peaked_units(handle, stream) -> int:
+    out = ctypes.c_int32()
+    check(lib.rtv_cache_peaked_units(handle, ctypes.byref(out), stream), "rtv_cache_peaked_units")
+    return out.value
 
 
 def rtv_ring_window(next_global_frame, committed, tokens_per_frame, chunk_frames, capacity_frames,

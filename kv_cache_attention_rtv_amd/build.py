@@ -1,6 +1,7 @@
 """Build the HIP library ``librtv.so`` in-tree for gfx950.
 
-Usage: python -m kv_cache_attention_rtv_amd.build   (or build() from Python)
+Usage: python kv_cache_attention_rtv_amd/build.py   (or build() from Python; run as a
+script, not with -m, which would import the package and so the library first)
 """
 from __future__ import annotations
 

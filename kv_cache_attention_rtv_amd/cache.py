@@ -24,14 +24,27 @@ class RtvConfig:
     capacity_frames: int
     max_global_frames: int
     rope_base: float = 10000.0
-    query_terms: int = 1        # 2: two-term e4m3 queries (keys with outlier channels)
-    prob_terms: int = 1         # 2: two-term attention weights on long windows (peaked attention)
+    query_terms: int = 1        # 2: two-term e4m3 queries on every window
+    prob_terms: int = 0         # 0: one-code weights checked for peaked rows (recomputed with two
+                                # terms); 1: one code, unchecked; 2: two terms on every window
+    # optional float32 [max_global_frames * T, D/2, 2] (cos, sin) table; None: the library's own
+    rope_table: object = None
 
     def to_c(self) -> abi.rtv_config:
-        return abi.rtv_config(self.n_layers, self.n_q_heads, self.n_kv_heads, self.head_dim,
-                              self.tokens_per_frame, self.chunk_frames, self.capacity_frames,
-                              self.max_global_frames, int(self.query_terms), int(self.prob_terms),
-                              float(self.rope_base))
+        table = None
+        if self.rope_table is not None:
+            import numpy as np
+
+            table = np.ascontiguousarray(self.rope_table, dtype=np.float32)
+            want = (self.max_global_frames * self.tokens_per_frame, self.head_dim // 2, 2)
+            if table.shape != want:
+                raise ValueError(f"rope_table must be {want}, got {table.shape}")
+        c = abi.rtv_config(self.n_layers, self.n_q_heads, self.n_kv_heads, self.head_dim,
+                           self.tokens_per_frame, self.chunk_frames, self.capacity_frames,
+                           self.max_global_frames, int(self.query_terms), int(self.prob_terms),
+                           float(self.rope_base), table.ctypes.data if table is not None else None)
+        c._table = table           # kept alive with the struct until the cache is created
+        return c
 
     @property
     def chunk_tokens(self) -> int:
@@ -115,6 +128,10 @@ class RtvCache:
 
     def window(self, layer: int, max_window_frames: int = 0) -> abi.rtv_window:
         return abi.rtv_cache_window(self.handle, layer, max_window_frames)
+
+    def peaked_units(self, stream=None) -> int:
+        """Query tiles the latest attend flagged as peaked and recomputed (synchronizes)."""
+        return abi.rtv_cache_peaked_units(self.handle, _stream(stream))
 
     def _view(self, ptr: int, nbytes: int) -> torch.Tensor:
         off = ptr - self.arena.data_ptr()

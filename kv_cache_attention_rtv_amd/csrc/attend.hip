@@ -12,7 +12,7 @@
 // a lone wave issues VALU instructions at about half the SIMD's rate, so two
 // waves in the same phase keep the VALU busy while the matrix-core phases of
 // both follow back to back.  The workgroup walks 64-key tiles of the
-// window's (at most two) slot segments through a 3-stage LDS ring with one
+// window's (at most two) slot segments through a 4-stage LDS ring with one
 // barrier per tile; waves 0-3 stage the K rows and waves 4-7 the V rows of
 // tile t+2 while tile t is computed.
 //
@@ -26,8 +26,11 @@
 //   brought to the PV operand layout by v_permlane16_swap (see there);
 //   O^T[d][query] += V^T . P'^T           D/32 d sub-tiles (32x32x64)
 //   L[r][query]   += U . P'^T             one product: the row sum
-// Scores: the queries of a workgroup share one e4m3 scale s_q, so the whole
-// per-score scale folds into a per-key factor kf = sk * s_q * log2(e)/sqrt(D).
+// Scores: each query carries its own power-of-two scale 2^e_q (its largest
+// rotated element maps into [128, 256)), applied exactly by the matrix core
+// through the E8M0 scale of the query operand, so the score products come out
+// in the units of the rotated query and the rest of the per-score scale is a
+// per-key factor kf = sk * log2(e)/sqrt(D) from the factors kernel.
 // P' carries the V scale of its key: P' = p * 55 * rho_key with
 // rho = sv / 2^e, 2^e the least power of two above the largest V scale of
 // the key's 64-slot tile; the PV product scales P' back by 2^e through the
@@ -47,6 +50,17 @@
 // running max m is lazy: it moves only when some P' would exceed 440, and
 // then leaves a factor 2^kTau of headroom.  Output O = acc / L, rounded to
 // bf16.
+//
+// Peaked rows.  The one-code P' (and one-term Q) errors, a few per cent per
+// weight, average out only when a row's weight spreads over many keys.  With
+// check_peaked the one-code kernels also take G = sum_k P'_k^2 per query on
+// the matrix cores (the diagonal of P' P'^T, one more product per tile whose
+// operands are the P' codes already in registers), and G / L^2 = sum_k
+// (p_k rho_k)^2 / (sum_k p_k)^2, a lower bound of sum p^2 over the normalised
+// weights, measures how few keys carry the row.  A unit (query tile x head)
+// with a row above kPeakedGram is flagged (for a key-range part, by the
+// combine kernel from the merged sums), and a second launch recomputes only
+// the flagged units with two-term Q and P' (relative error about 2^-8 each).
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "ring.hpp"
@@ -86,10 +100,16 @@ template <bool EXACT> struct LogUnits {
 constexpr float kPW = 55.0f;                // P' = p * kPW * rho, rho <= 1
 constexpr float kLogPW = 5.78135971f;       // log2(kPW)
 constexpr float kRhoMin = 0.0009765625f;    // 2^-10: floor of rho (U = 2^-2 / rho <= 256)
-constexpr float kScaleMin = 8.6736174e-19f; // 2^-60: floor of sk and of the query scale factor,
-                                            // so that kf >= 2^-120 and C stays finite
+constexpr float kScaleMin = 8.6736174e-19f; // 2^-60: floor of sk, so that C stays finite
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kMaskFactor = 1e30f;        // kf of a key outside the window segment
+// Peaked-row threshold on G / L^2 (sum over the window of (p rho)^2, p the
+// normalised weights).  Rows of N(0,1) queries and keys stay below 2.5e-5 on
+// a 47872-key window and 4e-4 on 8192 keys; simulated one-code errors stay
+// inside the attention tolerance below it, while every simulated row family
+// that breaks the tolerance (keys of a chunk scaled by 1.5 to 4, weight spread
+// evenly over 50-400 keys) lies above it.
+constexpr float kPeakedGram = 5e-4f;
 
 __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -251,14 +271,13 @@ __device__ __forceinline__ int vt_pos(int k) {
   return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);
 }
 
-// kscale = kUnit * max(s_q * log2(e) / sqrt(D), kScaleMin) (kf in the score
-// units), inv_kscale = 1 / max(s_q * log2(e) / sqrt(D), kScaleMin).
+// kunit: the score units per octave (kf is staged in those units).
 // The codes are stored branch-free apart from the masking of partial tiles:
 // K and V pieces differ only in their address.  The first K-side wave writes
 // kf and C (lane = key), lanes 0..7 of the first V-side wave the U rows.
 template <int D, bool MASK>
 __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, uint8_t* st,
-                                           float kscale, float inv_kscale, int tid) {
+                                           float kunit, int tid) {
   using SM = Smem<D>;
   constexpr int LD_BYTES = D / 4;
   const int gt = tid & 255;
@@ -288,8 +307,8 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, const TileRef& t, 
     // so u ~ -2e35 and P' = 0
     const int key = tid & 63;
     const bool ok = !MASK || (base + key >= t.lo && base + key < t.hi);
-    const float kf = __uint_as_float(xk.x) * kscale;
-    const float c = __uint_as_float(xk.y) * inv_kscale;
+    const float kf = __uint_as_float(xk.x) * kunit;
+    const float c = __uint_as_float(xk.y);
     float* kfp = (float*)(st + SM::KF_OFF);
     kfp[key] = ok ? kf : kMaskFactor;
     kfp[64 + key] = ok ? c : 0.0f;
@@ -314,10 +333,11 @@ __device__ __forceinline__ TileRef tile_of(int it, int t_count0, int t_first0, i
 // Per-window key factors: one wave per (KV head, window tile).  The tile's V
 // exponent e is the least power of two 2^e >= its largest V scale; for each
 // slot rho = sv / 2^e (exact; 1 for a zero V row, at least kRhoMin), the
-// record (sk' = max(sk, kScaleMin), log2(55 rho) / sk', 127 + e, 0) and the
-// two e4m3 terms of 2^-2 / rho at the slot's byte position in the U rows.
-// Slots of a partial tile outside the window get factors too (from whatever
-// their scales hold; the attention masks them).
+// record (kf = max(sk, kScaleMin) log2(e) / sqrt(D), log2(55 rho) / kf,
+// 127 + e, 0) and the two e4m3 terms of 2^-2 / rho at the slot's byte
+// position in the U rows.  Slots of a partial tile outside the window get
+// factors too (from whatever their scales hold; the attention masks them).
+// The first workgroup also clears the peaked-unit flags of the call.
 // Device-state mode: the window's segments, the chunk's RoPE rows and the
 // split schedule from the layer's ring state, with the same arithmetic as the
 // host's in host-state mode.  False, with the state's error set, when the
@@ -343,7 +363,10 @@ __device__ __forceinline__ bool attend_derive(AttendArgs& a) {
   return true;
 }
 
+template <int D>
 __global__ __launch_bounds__(256) void factors_kernel(AttendArgs a) {
+  if (a.flags && blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= a.n_work; i += 256) a.flags[i] = 0u;
   if (a.dstate && !attend_derive(a)) return;
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -372,10 +395,10 @@ __global__ __launch_bounds__(256) void factors_kernel(AttendArgs a) {
     e = e < -126 ? -126 : e;
   }
   const float rho = sv > 0.0f ? __builtin_fmaxf(ldexpf(sv, -e), kRhoMin) : 1.0f;
-  const float skf = __builtin_fmaxf(sk, kScaleMin);
+  const float kf = __builtin_fmaxf(sk, kScaleMin) * (kLog2e / sqrtf((float)D));
   const int64_t rt = (int64_t)h * a.ring_tiles + tile;
   ((float4*)a.fac_l)[rt * 64 + lane] =
-      make_float4(skf, (kLogPW + __builtin_amdgcn_logf(rho)) / skf, __uint_as_float((uint32_t)(127 + e)), 0.0f);
+      make_float4(kf, (kLogPW + __builtin_amdgcn_logf(rho)) / kf, __uint_as_float((uint32_t)(127 + e)), 0.0f);
   const float u = 0.25f / rho;
   const int hi = __builtin_amdgcn_cvt_pk_fp8_f32(u, 0.0f, 0, false);
   const float uh = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false)[0];
@@ -419,8 +442,9 @@ __device__ __forceinline__ float max32(const float (&t)[32]) {
 // P' of the row at 440 / 2^kTau.  m is finite from the first tile on (set
 // from tile 0 before the loop), so the raw row max is max(u) + m and no
 // score is recomputed.
-template <int NDT, class LU>
-__device__ __forceinline__ void lazy_rescale(float mx, float& m, v16f (&o)[NDT], v16f& lsum, float (&t)[32]) {
+template <int NDT, class LU, bool STAT>
+__device__ __forceinline__ void lazy_rescale(float mx, float& m, v16f (&o)[NDT], v16f& lsum, v16f& gsum,
+                                             float (&t)[32]) {
   if (__builtin_expect(__any(mx > LU::kTop), 0)) {
     const float raw = xhalf_max(mx) + m;
     const float m_new = __builtin_fmaxf(m, raw - LU::kReset);
@@ -429,6 +453,7 @@ __device__ __forceinline__ void lazy_rescale(float mx, float& m, v16f (&o)[NDT],
 #pragma unroll
     for (int d = 0; d < NDT; ++d) o[d] *= alpha;
     lsum *= alpha;
+    if constexpr (STAT) gsum *= alpha * alpha;
 #pragma unroll
     for (int j = 0; j < 32; ++j) t[j] += shift;
     m = m_new;
@@ -479,6 +504,9 @@ __device__ __forceinline__ bool work_item(const AttendArgs& a, int& unit, int& p
     part = -1;
     return unit < a.n_full;
   }
+  // (device-state grids are sized for the largest window: surplus workgroups
+  // of an XCD leave instead of taking another XCD's parts)
+  if (local - a.full_per_xcd >= a.parts_per_xcd) return false;
   const int j = xcd * a.parts_per_xcd + (local - a.full_per_xcd);
   if (j >= a.n_parts) return false;
   unit = a.n_full + j / a.parts_per_unit;
@@ -486,53 +514,43 @@ __device__ __forceinline__ bool work_item(const AttendArgs& a, int& unit, int& p
   return true;
 }
 
-// max |q| of the rotated query row `row` (clamped to the chunk) over the RoPE
-// pairs [P hh, P hh + P) of lane half hh, both halves of each pair
-template <int D>
-__device__ __forceinline__ float lane_q_amax(const AttendArgs& a, int row, int head, int hh) {
-  constexpr int P = D / 4;
-  const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
-  const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
-  const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
-  float m = 0.0f;
-#pragma unroll
-  for (int j = 0; j < P; j += 8) {
-    const uint4 w0 = *(const uint4*)(q_src + P * hh + j);
-    const uint4 w1 = *(const uint4*)(q_src + D / 2 + P * hh + j);
-    const uint32_t x0w[4] = {w0.x, w0.y, w0.z, w0.w};
-    const uint32_t x1w[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
-      const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
-      const float2 c = *(const float2*)(q_cs + 2 * (j + e));
-      const float r0 = x0 * c.x - x1 * c.y;
-      const float r1 = x1 * c.x + x0 * c.y;
-      m = __builtin_fmaxf(m, __builtin_fmaxf(fabsf(r0), fabsf(r1)));
-    }
+// E8M0 exponent e of a query's power-of-two scale: its largest rotated |q|
+// divided by 2^e lies in [128, 256) (e4m3 reaches 448).  Clamped so that both
+// terms of a two-term query keep their E8M0 scales in range (an all-zero query
+// takes 2^0).
+__device__ __forceinline__ int query_exp(float amax) {
+  int e = 0;
+  if (amax > 0.0f) {
+    (void)frexpf(amax, &e);             // amax = f 2^e, f in [0.5, 1)
+    e -= 8;
   }
-  return m;
+  return e < -120 ? -120 : (e > 120 ? 120 : e);
 }
 
-// The workgroup's max of x (one barrier; red holds one value per wave)
-__device__ __forceinline__ float wg_max(float x, float* red, int wave, int lane) {
+// G of query li of the lane (PV layout): the diagonal element (li, li) of the
+// 32x32 product P' P'^T sits in lane 32 ((li >> 2) & 1) + li, register
+// 4 (li >> 3) + (li & 3); both lanes of the query receive it.
+__device__ __forceinline__ float gram_diag(const v16f& g, int li, int hh) {
+  const int gi = 4 * (li >> 3) + (li & 3);
+  float x = 0.0f;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, o));
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  x = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) x = __builtin_fmaxf(x, red[w]);
-  return x;
+  for (int i = 0; i < 16; ++i) x = i == gi ? g[i] : x;
+  return xhalf_sum(hh == ((li >> 2) & 1) ? x : 0.0f);
+}
+
+// flag a unit as peaked; the first flag of a unit counts it
+__device__ __forceinline__ void flag_unit(const AttendArgs& a, int unit) {
+  if (atomicOr(&a.flags[unit], 1u) == 0u) atomicAdd(&a.flags[a.n_work], 1u);
 }
 
 // Result of one lane for its query (PV layout: lane (hh, li) holds query li
 // of a 32-query sub-tile, q its index in the workgroup): a whole unit writes O
-// = acc / L as bf16; a key-range part writes sum p V / 55 and (m, sum p / 55)
-// with m back in log2 units (u = kUnit t + kOff, so m = (m_u + kOff) / kUnit).
+// = acc / L as bf16; a key-range part writes sum p V / 55 and (m, sum p / 55,
+// sum p'^2 / 55^2) with m back in log2 units (u = kUnit t + kOff, so m =
+// (m_u + kOff) / kUnit).
 template <int D, class LU>
 __device__ __forceinline__ void write_result(const AttendArgs& a, const v16f (&o)[D / 32], float l_tot, float m_u,
-                                             int part, int q, int row, int head, int hh) {
+                                             float g, int part, int q, int row, int head, int hh) {
   constexpr int NDT = D / 32;
   if (part >= 0) {
     float* po = a.ws_o + ((int64_t)part * kQPB + q) * D;
@@ -546,8 +564,8 @@ __device__ __forceinline__ void write_result(const AttendArgs& a, const v16f (&o
                                           o[d][4 * g + 2] * inv_c, o[d][4 * g + 3] * inv_c);
       }
     if (hh == 0)
-      *(float2*)(a.ws_ml + ((int64_t)part * kQPB + q) * 2) =
-          make_float2((m_u + LU::kOff) * (1.0f / LU::kUnit), l_tot / kPW);
+      *(float4*)(a.ws_ml + ((int64_t)part * kQPB + q) * 4) =
+          make_float4((m_u + LU::kOff) * (1.0f / LU::kUnit), l_tot / kPW, g * (1.0f / (kPW * kPW)), 0.0f);
     return;
   }
   const float scale = 1.0f / l_tot;
@@ -577,8 +595,10 @@ __device__ __forceinline__ void write_result(const AttendArgs& a, const v16f (&o
 // rounding error of Q moves every score of a row coherently and is amplified
 // by large K channels: short windows always carry QLO, longer ones when the
 // cache was created for two query terms (keys with outlier channels).
-template <int D, bool MASK, bool QLO, bool PLO>
+template <int D, bool MASK, bool QLO, bool PLO, bool STAT>
 __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(AttendArgs a) {
+  static_assert(!(STAT && PLO), "the peaked-row check serves the one-code kernels");
+  if (a.redo && a.flags[a.n_work] == 0u) return;      // no unit flagged
   if (a.dstate && !attend_derive(a)) return;
   using SM = Smem<D>;
   using LU = LogUnits<PLO>;
@@ -586,10 +606,10 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   constexpr int NDT = D / 32;               // 32-row d sub-tiles of O^T
   constexpr int P = D / 4;                  // RoPE pairs per lane
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * SM::STAGE];
-  __shared__ float red[kWaves];
 
   int unit, part;
   if (!work_item(a, unit, part)) return;
+  if (a.redo && a.flags[unit] == 0u) return;
   const int head = unit / a.n_qtiles;
   const int qtile = unit % a.n_qtiles;
   const int kvh = head / a.group;
@@ -608,32 +628,23 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   const int k_off = k_code_off<D>(tid & 255), v_off = v_code_off<D>(tid & 255);
   const int xk_off = (tid & 63) * 16, xv_off = (tid & 7) * 16;
 
-  // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
+  // ---- Q prologue: RoPE, the query's power-of-two scale, e4m3 codes in the
+  // B-operand layout.  Operand step s, byte b <-> d: D=128: d = 64 s + 32 hh +
+  // b; D=64: byte b < 16 -> d = 16 hh + b, b >= 16 -> d = 32 + 16 hh + b - 16
+  // (RoPE pairs stay in-lane); lanes li and li + 32 hold one query
   int q_rows[kSub];
-  float qamax = 0.0f;
-#pragma unroll
-  for (int sub = 0; sub < kSub; ++sub) {
-    q_rows[sub] = qtile * kQPB + wave * kQPW + sub * 32 + li;
-    qamax = __builtin_fmaxf(qamax, lane_q_amax<D>(a, q_rows[sub], head, hh));
-  }
-  qamax = wg_max(qamax, red, wave, lane);
-  const float q_inv = qamax > 0.0f ? kFp8Max / qamax : 0.0f;
-  const float kscale = __builtin_fmaxf((qamax / kFp8Max) * (kLog2e / sqrtf((float)D)), kScaleMin);
-  const float inv_kscale = 1.0f / kscale;
-  const float kscale_u = kscale * LU::kUnit;  // kf in the score units (C stays in raw units)
-
-  // ---- Q prologue pass 2: e4m3 codes in the B-operand layout ---------------
-  // operand step s, byte b <-> d: D=128: d = 64 s + 32 hh + b; D=64: byte b < 16
-  // -> d = 16 hh + b, b >= 16 -> d = 32 + 16 hh + b - 16 (RoPE pairs stay in-lane)
+  int qexp[kSub];                           // E8M0 scale of the lane's query
   v8i qop[kSub][NSTEP];
   v8i qlo[kSub][NSTEP];
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub) {
-    const int row = q_rows[sub];
+    const int row = qtile * kQPB + wave * kQPW + sub * 32 + li;
+    q_rows[sub] = row;
     const int src_row = row < a.n_tokens ? row : a.n_tokens - 1;
     const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
     const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * hh) * 2;
     float r0[P], r1[P];
+    float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < P; j += 8) {
       const uint4 w0 = *(const uint4*)(q_src + P * hh + j);
@@ -645,18 +656,21 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
         const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
         const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
         const float2 c = *(const float2*)(q_cs + 2 * (j + e));
-        r0[j + e] = (x0 * c.x - x1 * c.y) * q_inv;
-        r1[j + e] = (x1 * c.x + x0 * c.y) * q_inv;
+        r0[j + e] = x0 * c.x - x1 * c.y;
+        r1[j + e] = x1 * c.x + x0 * c.y;
+        amax = __builtin_fmaxf(amax, __builtin_fmaxf(fabsf(r0[j + e]), fabsf(r1[j + e])));
       }
     }
+    const int e = query_exp(xhalf_max(amax));
+    qexp[sub] = 127 + e;
 #pragma unroll
     for (int w = 0; w < NSTEP * 8; ++w) {
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int b = 4 * w + e;
-        if constexpr (D == 128) v[e] = (b < 32) ? r0[b] : r1[b - 32];
-        else v[e] = (b < 16) ? r0[b] : r1[b - 16];
+      for (int k = 0; k < 4; ++k) {
+        const int b = 4 * w + k;
+        const float x = (D == 128) ? ((b < 32) ? r0[b] : r1[b - 32]) : ((b < 16) ? r0[b] : r1[b - 16]);
+        v[k] = __builtin_amdgcn_ldexpf(x, -e);   // exact
       }
       uint32_t c = 0, lo = 0;
       if constexpr (QLO) {
@@ -727,8 +741,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   };
   auto qk_step = [&](int j, int sub, const v8i (&kop)[2][NSTEP], v16f (&acc)[2]) {
     const int kh = j & 1, s = j >> 1;
-    acc[kh] = mfma_fp8(kop[kh][s], qop[sub][s], acc[kh]);
-    if constexpr (QLO) acc[kh] = mfma_fp8_bscaled(kop[kh][s], qlo[sub][s], acc[kh], 127 - kLoShift);
+    acc[kh] = mfma_fp8_bscaled(kop[kh][s], qop[sub][s], acc[kh], qexp[sub]);
+    if constexpr (QLO) acc[kh] = mfma_fp8_bscaled(kop[kh][s], qlo[sub][s], acc[kh], qexp[sub] - kLoShift);
   };
   // keys of tile it outside its segment: add -448 * 448 to their raw scores
   // with one MFMA per key half (A: -448 at one k position of a masked key row,
@@ -753,11 +767,13 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
   // the V products scale it back by the E8M0 exponent ev = 127 + e.)
   v16f acc_o[kSub][NDT];
   v16f acc_l[kSub];
+  v16f acc_g[kSub];                         // P' P'^T (peaked-row check)
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub) {
 #pragma unroll
     for (int d = 0; d < NDT; ++d) acc_o[sub][d] = v16f{};
     acc_l[sub] = v16f{};
+    acc_g[sub] = v16f{};
   }
   const int u_off = SM::U_OFF + (li < 2 ? li : 2) * SM::VROW + 32 * hh;
   auto load_v = [&](const uint8_t* st, v8i (&vop)[NDT + 1]) {
@@ -779,6 +795,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     } else {
       acc_l[sub] = mfma_fp8_scaled(vop[NDT], pop[sub], acc_l[sub], 127 + 2, 127);
       if constexpr (PLO) acc_l[sub] = mfma_fp8_scaled(vop[NDT], plo[sub], acc_l[sub], 127 + 2, 127 - kLoShift);
+      if constexpr (STAT) acc_g[sub] = mfma_fp8(pop[sub], pop[sub], acc_g[sub]);
     }
   };
 
@@ -791,7 +808,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       load_tile<D>(regs, tref(clamp_it(p)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
-      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale_u, inv_kscale, tid);
+      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), LU::kUnit, tid);
     }
     load_tile<D>(regs, tref(clamp_it(2)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
   }
@@ -835,7 +852,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     // next one) and the loads of tile it + 3; at the top of the iteration so
     // that its latency overlaps the products.  Unconditional with the tile
     // index clamped: past the end the copy lands in a stage nobody reads again
-    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(r + 2), kscale_u, inv_kscale, tid);
+    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(r + 2), LU::kUnit, tid);
     load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
 
     // (1) the PV and row-sum products of tile it - 1, interleaved with the
@@ -870,7 +887,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     for (int sub = 0; sub < kSub; ++sub) {
       // (any lane over the bound triggers: no cross-half max needed here)
       const float mx = max32(t[sub]);
-      lazy_rescale<NDT, LU>(mx, m_run[sub], acc_o[sub], acc_l[sub], t[sub]);
+      lazy_rescale<NDT, LU, STAT>(mx, m_run[sub], acc_o[sub], acc_l[sub], acc_g[sub], t[sub]);
     }
 
     // (2) the score products of tile it + 1 (past the last tile they read a
@@ -919,7 +936,11 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
     // row sum: rows 0 and 1 of L (registers 0 and 1 of the lanes hh = 0; the
     // same registers of the lanes hh = 1 hold the zero rows 4 and 5)
     const float l_tot = xhalf_sum(acc_l[sub][0] + acc_l[sub][1]);
-    write_result<D, LU>(a, acc_o[sub], l_tot, m_run[sub], part, wave * kQPW + sub * 32 + li, q_rows[sub], head, hh);
+    const float g = STAT ? gram_diag(acc_g[sub], li, hh) : 0.0f;
+    write_result<D, LU>(a, acc_o[sub], l_tot, m_run[sub], g, part, wave * kQPW + sub * 32 + li, q_rows[sub], head,
+                        hh);
+    if constexpr (STAT)
+      if (part < 0 && __any(g > kPeakedGram * l_tot * l_tot) && lane == 0) flag_unit(a, unit);
   }
 }
 
@@ -965,20 +986,22 @@ __device__ __forceinline__ float max16(const float (&t)[4][4]) {
                          __builtin_fmaxf(__builtin_fmaxf(a[3], a[4]), a[5]));
 }
 
-template <bool MASK, bool QLO, bool PLO>
+template <bool MASK, bool QLO, bool PLO, bool STAT>
 __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kernel(AttendArgs a) {
   static_assert(kSub == 1, "one 32-query sub-tile per wave");
+  static_assert(!(STAT && PLO), "the peaked-row check serves the one-code kernels");
   constexpr int D = 128;
+  if (a.redo && a.flags[a.n_work] == 0u) return;      // no unit flagged
   if (a.dstate && !attend_derive(a)) return;
   using SM = Smem<D>;
   using LU = LogUnits<PLO>;
   constexpr int NDT = D / 32;               // 32-row d sub-tiles of O^T
   constexpr int P = D / 4;                  // RoPE pairs per lane
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * SM::STAGE];
-  __shared__ float red[kWaves];
 
   int unit, part;
   if (!work_item(a, unit, part)) return;
+  if (a.redo && a.flags[unit] == 0u) return;
   const int head = unit / a.n_qtiles;
   const int qtile = unit % a.n_qtiles;
   const int kvh = head / a.group;
@@ -999,18 +1022,13 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
   const int k_off = k_code_off<D>(tid & 255), v_off = v_code_off<D>(tid & 255);
   const int xk_off = (tid & 63) * 16, xv_off = (tid & 7) * 16;
 
-  // ---- Q prologue pass 1: RoPE and the workgroup's max |q| ----------------
-  const int wrow = qtile * kQPB + wave * kQPW;  // first query row of the wave
-  const float qamax = wg_max(lane_q_amax<D>(a, wrow + li, head, hh), red, wave, lane);
-  const float q_inv = qamax > 0.0f ? kFp8Max / qamax : 0.0f;
-  const float kscale = __builtin_fmaxf((qamax / kFp8Max) * (kLog2e / sqrtf((float)D)), kScaleMin);
-  const float inv_kscale = 1.0f / kscale;
-  const float kscale_u = kscale * LU::kUnit;  // kf in the score units (C stays in raw units)
-
-  // ---- Q prologue pass 2: e4m3 codes in the 16x16x128 B-operand layout ------
+  // ---- Q prologue: RoPE, each query's power-of-two scale (over the four
+  // lanes that hold it) and e4m3 codes in the 16x16x128 B-operand layout:
   // lane (q4, i), query block qb: query 16 qb + i, byte b <-> d = 32 q4 + b
   // (q4 & 1 selects the RoPE pair block, q4 >> 1 the half of the pair)
+  const int wrow = qtile * kQPB + wave * kQPW;  // first query row of the wave
   v8i qop[2], qlo[2];
+  int qexp[2];                              // E8M0 scale of the lane's query of block qb
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = wrow + 16 * qb + i16;
@@ -1020,6 +1038,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
     const uint16_t* q_src = a.q + (int64_t)src_row * a.ldq + (int64_t)head * D;
     const float* q_cs = a.rope + ((int64_t)src_row * (D / 2) + P * pb) * 2;
     float v[P];
+    float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < P; j += 8) {
       const uint4 w0 = *(const uint4*)(q_src + P * pb + j);
@@ -1031,11 +1050,16 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
         const float x0 = (e & 1) ? bf16_hi(x0w[e >> 1]) : bf16_lo(x0w[e >> 1]);
         const float x1 = (e & 1) ? bf16_hi(x1w[e >> 1]) : bf16_lo(x1w[e >> 1]);
         const float2 c = *(const float2*)(q_cs + 2 * (j + e));
-        const float r0 = (x0 * c.x - x1 * c.y) * q_inv;
-        const float r1 = (x1 * c.x + x0 * c.y) * q_inv;
+        const float r0 = x0 * c.x - x1 * c.y;
+        const float r1 = x1 * c.x + x0 * c.y;
         v[j + e] = upper ? r1 : r0;
+        amax = __builtin_fmaxf(amax, fabsf(v[j + e]));
       }
     }
+    const int e = query_exp(quad_max(amax));
+    qexp[qb] = 127 + e;
+#pragma unroll
+    for (int j = 0; j < P; ++j) v[j] = __builtin_amdgcn_ldexpf(v[j], -e);   // exact
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       uint32_t c = 0, lo = 0;
@@ -1098,8 +1122,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
   auto qk_step = [&](int kb, const v8i (&kop)[4], const v4f (&cin)[4], v4f (&acc)[4][2]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      acc[kb][qb] = mfma16_fp8(kop[kb], qop[qb], cin[kb]);
-      if constexpr (QLO) acc[kb][qb] = mfma16_fp8_bscaled(kop[kb], qlo[qb], acc[kb][qb], 127 - kLoShift);
+      acc[kb][qb] = mfma16_fp8_bscaled(kop[kb], qop[qb], cin[kb], qexp[qb]);
+      if constexpr (QLO) acc[kb][qb] = mfma16_fp8_bscaled(kop[kb], qlo[qb], acc[kb][qb], qexp[qb] - kLoShift);
     }
   };
   // keys of tile it outside its segment: add -448 * 448 to their raw scores
@@ -1122,6 +1146,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
   // O^T += V^T . P'^T and the row sum, as in attend_kernel
   v16f acc_o[NDT];
   v16f acc_l = v16f{};
+  v16f acc_g = v16f{};                      // P' P'^T (peaked-row check)
 #pragma unroll
   for (int d = 0; d < NDT; ++d) acc_o[d] = v16f{};
   const int u_off = SM::U_OFF + (li < 2 ? li : 2) * SM::VROW + 32 * hh;
@@ -1142,6 +1167,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
     } else {
       acc_l = mfma_fp8_scaled(vop[NDT], pop, acc_l, 127 + 2, 127);
       if constexpr (PLO) acc_l = mfma_fp8_scaled(vop[NDT], plo, acc_l, 127 + 2, 127 - kLoShift);
+      if constexpr (STAT) acc_g = mfma_fp8(pop, pop, acc_g);
     }
   };
   // P' of key block kb (chunk kb of the second half): codes of both query
@@ -1183,7 +1209,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       load_tile<D>(regs, tref(clamp_it(p)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
-      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), kscale_u, inv_kscale, tid);
+      store_tile<D, MASK>(regs, tref(clamp_it(p)), stage_of(p), LU::kUnit, tid);
     }
     load_tile<D>(regs, tref(clamp_it(2)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
   }
@@ -1222,7 +1248,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
 
   auto tile_step = [&](const int it, const int r) __attribute__((always_inline)) {
     // (0) staging of tile it + 2 and the loads of tile it + 3 (as in attend_kernel)
-    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(r + 2), kscale_u, inv_kscale, tid);
+    store_tile<D, MASK>(regs, tref(clamp_it(it + 2)), stage_of(r + 2), LU::kUnit, tid);
     load_tile<D>(regs, tref(clamp_it(it + 3)), kc, vc, frec, fu, side, k_off, v_off, xk_off, xv_off);
 
     // (1) the PV and row-sum products of tile it - 1, interleaved with the
@@ -1275,6 +1301,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
 #pragma unroll
         for (int d = 0; d < NDT; ++d) acc_o[d] *= al;
         acc_l *= al;
+        if constexpr (STAT) acc_g *= al * al;
       }
     }
 
@@ -1312,24 +1339,31 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
 
   // ---- epilogue (PV layout: lane (hh, li) holds query li, the query block q4 & 1)
   const float l_tot = xhalf_sum(acc_l[0] + acc_l[1]);
-  write_result<D, LU>(a, acc_o, l_tot, (q4 & 1) ? m_run[1] : m_run[0], part, wave * kQPW + li, wrow + li, head, hh);
+  const float g = STAT ? gram_diag(acc_g, li, hh) : 0.0f;
+  write_result<D, LU>(a, acc_o, l_tot, (q4 & 1) ? m_run[1] : m_run[0], g, part, wave * kQPW + li, wrow + li, head,
+                      hh);
+  if constexpr (STAT)
+    if (part < 0 && __any(g > kPeakedGram * l_tot * l_tot) && lane == 0) flag_unit(a, unit);
 }
 
 // Merge the key-range parts of the split units: for each query,
 // M = max_p m_p, w_p = 2^(m_p - M), O = sum_p w_p O_p / sum_p w_p l_p.
-// One workgroup = kCombineQ queries of one split unit (blockIdx.x: the unit,
-// blockIdx.y: the query group), kCombineT threads per query with D /
-// kCombineT dimensions each: a query's partial rows are read as contiguous
+// With the peaked-row check the merged G = sum_p w_p^2 g_p against L^2 flags
+// the unit.  One workgroup = kCombineQ queries of one split unit (blockIdx.x:
+// the unit, blockIdx.y: the query group), kCombineT threads per query with D
+// / kCombineT dimensions each: a query's partial rows are read as contiguous
 // runs and the whole device takes part.
 constexpr int kCombineQ = 16;
 constexpr int kCombineT = 16;
 template <int D>
 __global__ __launch_bounds__(kCombineQ * kCombineT) void combine_kernel(AttendArgs a) {
+  if (a.redo && a.flags[a.n_work] == 0u) return;      // no unit flagged
   if (a.dstate && !attend_derive(a)) return;
   constexpr int DT = D / kCombineT;               // dimensions per thread
   const int r = blockIdx.x;                       // split unit r
   if (a.n_full + r >= a.n_work) return;           // (device-state grids cover the most split units)
   const int unit = a.n_full + r;
+  if (a.redo && a.flags[unit] == 0u) return;
   const int head = unit / a.n_qtiles;
   const int qtile = unit % a.n_qtiles;
   const int S = a.parts_per_unit;
@@ -1339,15 +1373,16 @@ __global__ __launch_bounds__(kCombineQ * kCombineT) void combine_kernel(AttendAr
   if (row >= a.n_tokens) return;
   const int j0 = r * S;
   float M = -INFINITY;
-  for (int p = 0; p < S; ++p) M = fmaxf(M, a.ws_ml[((int64_t)(j0 + p) * kQPB + q) * 2]);
-  float L = 0.0f;
+  for (int p = 0; p < S; ++p) M = fmaxf(M, a.ws_ml[((int64_t)(j0 + p) * kQPB + q) * 4]);
+  float L = 0.0f, G = 0.0f;
   float acc[DT];
 #pragma unroll
   for (int d = 0; d < DT; ++d) acc[d] = 0.0f;
   for (int p = 0; p < S; ++p) {
-    const float2 ml = *(const float2*)(a.ws_ml + ((int64_t)(j0 + p) * kQPB + q) * 2);
+    const float4 ml = *(const float4*)(a.ws_ml + ((int64_t)(j0 + p) * kQPB + q) * 4);
     const float w = exp2f(ml.x - M);
     L += w * ml.y;
+    G += w * w * ml.z;
     const float* po = a.ws_o + ((int64_t)(j0 + p) * kQPB + q) * D + d0;
 #pragma unroll
     for (int d = 0; d < DT; d += 4) {
@@ -1355,6 +1390,7 @@ __global__ __launch_bounds__(kCombineQ * kCombineT) void combine_kernel(AttendAr
       acc[d] += w * o.x; acc[d + 1] += w * o.y; acc[d + 2] += w * o.z; acc[d + 3] += w * o.w;
     }
   }
+  if (a.check_peaked && !a.redo && d0 == 0 && G > kPeakedGram * L * L) flag_unit(a, unit);
   const float inv = 1.0f / L;
   uint16_t* dst = a.out + (int64_t)row * a.ldo + (int64_t)head * D + d0;
 #pragma unroll
@@ -1373,14 +1409,16 @@ int attend_queries_per_block() { return kQPB; }
 int attend_max_parts() { return kMaxParts; }
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 static size_t partials_bytes(int head_dim) {
-  return align256((size_t)kMaxParts * kQPB * ((size_t)head_dim + 2) * sizeof(float));
+  return align256((size_t)kMaxParts * kQPB * ((size_t)head_dim + 4) * sizeof(float));
 }
-size_t attend_workspace_bytes(int head_dim, int n_kv_heads, int64_t slots_padded) {
+size_t attend_workspace_bytes(int head_dim, int n_kv_heads, int64_t slots_padded, int64_t n_units) {
   const size_t tiles = (size_t)n_kv_heads * (size_t)(slots_padded / 64);
-  return partials_bytes(head_dim) + align256(tiles * 64 * 16) +
-         align256(tiles * 128);
+  return partials_bytes(head_dim) + align256(tiles * 64 * 16) + align256(tiles * 128) +
+         align256(((size_t)n_units + 1) * sizeof(uint32_t));
 }
-void attend_set_workspace(AttendArgs& a, void* ws, int head_dim, int n_kv_heads, int64_t slots_padded) {
+void attend_set_workspace(AttendArgs& a, void* ws, int head_dim, int n_kv_heads, int64_t slots_padded,
+                          int64_t n_units) {
+  (void)n_units;
   uint8_t* p = static_cast<uint8_t*>(ws);
   const size_t tiles = (size_t)n_kv_heads * (size_t)(slots_padded / 64);
   a.ws_o = reinterpret_cast<float*>(p);
@@ -1389,6 +1427,8 @@ void attend_set_workspace(AttendArgs& a, void* ws, int head_dim, int n_kv_heads,
   a.fac_l = reinterpret_cast<float*>(p);
   p += align256(tiles * 64 * 16);
   a.fac_u = p;
+  p += align256(tiles * 128);
+  a.flags = reinterpret_cast<uint32_t*>(p);
   a.n_kv_heads = n_kv_heads;
   a.ring_tiles = (int32_t)(slots_padded / 64);
 }
@@ -1399,13 +1439,39 @@ hipError_t attend_capacity(int* workgroups) {
   hipDeviceProp_t prop;
   if (e == hipSuccess) e = hipGetDeviceProperties(&prop, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend16_kernel<false, false, false>, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend16_kernel<false, false, false, true>, kThreads,
+                                                     0);
   if (e != hipSuccess) return e;
   *workgroups = (per_cu > 0 ? per_cu : 1) * prop.multiProcessorCount;
   return hipSuccess;
 }
 
-hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t stream) {
+namespace {
+
+template <int D, bool MASK, bool QL, bool PL, bool ST>
+void launch_one(const dim3& g, const dim3& b, const AttendArgs& a, hipStream_t s) {
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((attend16_kernel<MASK, QL, PL, ST>), g, b, 0, s, a);
+  else
+    hipLaunchKernelGGL((attend_kernel<D, MASK, QL, PL, ST>), g, b, 0, s, a);
+}
+
+// the attention kernel variant: two-term Q and P' (precise), two-term Q with
+// one-code P', or one-term Q with one-code P'; the one-code variants with or
+// without the peaked-row check
+template <int D, bool MASK>
+void launch_variant(bool precise, bool two_term_q, bool check, const dim3& g, const dim3& b, const AttendArgs& a,
+                    hipStream_t s) {
+  if (precise)
+    launch_one<D, MASK, true, true, false>(g, b, a, s);
+  else if (two_term_q)
+    check ? launch_one<D, MASK, true, false, true>(g, b, a, s) : launch_one<D, MASK, true, false, false>(g, b, a, s);
+  else
+    check ? launch_one<D, MASK, false, false, true>(g, b, a, s) : launch_one<D, MASK, false, false, false>(g, b, a, s);
+}
+
+template <int D>
+hipError_t launch_attend_d(const AttendArgs& args_in, hipStream_t stream) {
   AttendArgs args = args_in;
   bool aligned = true, short_window = false;
   int n_tiles = 0, grid_per_xcd = 0, rem = 0;
@@ -1424,7 +1490,9 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
     // Device-state mode: the kernels derive the window and the schedule, so
     // the variant and the grids are fixed by the ring's shape.  Every window
     // holds at least one chunk and starts on a chunk boundary when the cap
-    // is a multiple of the chunk; the grids cover the largest window.
+    // is a multiple of the chunk; the grids cover the largest window.  The
+    // variant follows the shortest window (one chunk): a ring whose chunk is
+    // under 8192 keys takes the two-term kernel on every window.
     const RingShape& sh = args.shape;
     const int64_t chunk = (int64_t)sh.chunk_frames * sh.tokens_per_frame;
     aligned = chunk % 64 == 0 && sh.max_window_frames % sh.chunk_frames == 0;
@@ -1438,46 +1506,46 @@ hipError_t launch_attend(const AttendArgs& args_in, int head_dim, hipStream_t st
     rem = most.n_work - most.n_full;
   }
   const bool two_term_q = short_window || args.two_term_q;
+  const bool check = !short_window && args.check_peaked;
+  args.check_peaked = check ? 1 : 0;
+  args.redo = 0;
   {
     const int waves = n_tiles * args.n_kv_heads;
-    if (waves > 0) hipLaunchKernelGGL(factors_kernel, dim3((waves + 3) / 4), dim3(256), 0, stream, args);
+    if (waves > 0) hipLaunchKernelGGL(factors_kernel<D>, dim3((waves + 3) / 4), dim3(256), 0, stream, args);
   }
   const dim3 g(8 * grid_per_xcd), b(kThreads);
-#define RTV_LAUNCH(DIM, MASK, QL, PL) \
-  hipLaunchKernelGGL((attend_kernel<DIM, MASK, QL, PL>), g, b, 0, stream, args)
-#define RTV_DISPATCH_MASK(DIM, QL, PL) \
-  if (aligned) RTV_LAUNCH(DIM, false, QL, PL); else RTV_LAUNCH(DIM, true, QL, PL);
-#define RTV_DISPATCH(DIM)                                 \
-  if (short_window) {                                     \
-    RTV_DISPATCH_MASK(DIM, true, true)                    \
-  } else if (two_term_q) {                                \
-    RTV_DISPATCH_MASK(DIM, true, false)                   \
-  } else {                                                \
-    RTV_DISPATCH_MASK(DIM, false, false)                  \
-  }
-  // head dim 128: attend16_kernel (16x16x128 score products); 64: attend_kernel
-  if (head_dim == 128) {
-#undef RTV_LAUNCH
-#define RTV_LAUNCH(DIM, MASK, QL, PL) \
-  hipLaunchKernelGGL((attend16_kernel<MASK, QL, PL>), g, b, 0, stream, args)
-    RTV_DISPATCH(128)
-  } else {
-#undef RTV_LAUNCH
-#define RTV_LAUNCH(DIM, MASK, QL, PL) \
-  hipLaunchKernelGGL((attend_kernel<DIM, MASK, QL, PL>), g, b, 0, stream, args)
-    RTV_DISPATCH(64)
-  }
-#undef RTV_DISPATCH
-#undef RTV_DISPATCH_MASK
-#undef RTV_LAUNCH
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || rem == 0) return e;
-  const dim3 cg(rem, kQPB / kCombineQ), cb(kCombineQ * kCombineT);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(combine_kernel<128>, cg, cb, 0, stream, args);
+  if (aligned)
+    launch_variant<D, false>(short_window, two_term_q, check, g, b, args, stream);
   else
-    hipLaunchKernelGGL(combine_kernel<64>, cg, cb, 0, stream, args);
-  return hipGetLastError();
+    launch_variant<D, true>(short_window, two_term_q, check, g, b, args, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 cg(rem, kQPB / kCombineQ), cb(kCombineQ * kCombineT);
+  if (rem > 0) {
+    hipLaunchKernelGGL(combine_kernel<D>, cg, cb, 0, stream, args);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (!check) return hipSuccess;
+  // recompute the units flagged as peaked with two-term Q and P' (every
+  // workgroup of these launches exits at once when none is flagged)
+  AttendArgs redo = args;
+  redo.redo = 1;
+  if (aligned)
+    launch_one<D, false, true, true, false>(g, b, redo, stream);
+  else
+    launch_one<D, true, true, true, false>(g, b, redo, stream);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (rem > 0) {
+    hipLaunchKernelGGL(combine_kernel<D>, cg, cb, 0, stream, redo);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+hipError_t launch_attend(const AttendArgs& args, int head_dim, hipStream_t stream) {
+  return head_dim == 128 ? launch_attend_d<128>(args, stream) : launch_attend_d<64>(args, stream);
 }
 
 }  // namespace rtv

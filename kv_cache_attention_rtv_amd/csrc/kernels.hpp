@@ -71,6 +71,9 @@ struct AttendArgs {
   int32_t capacity;       // workgroups the device runs concurrently (0 = never split)
   int32_t two_term_q;     // queries as two e4m3 terms on every window
   int32_t two_term_p;     // P' (and queries) as two e4m3 terms on every window
+  int32_t check_peaked;   // one-code P' windows are checked for peaked rows and
+                          // the flagged units recomputed with two-term Q and P'
+  int32_t redo;           // this launch recomputes only the units flagged in `flags`
   // schedule (filled by launch_attend): units [0, n_full) run whole windows; units [n_full, n_work) are
   // split into parts_per_unit key ranges whose partial (O, m, l) go to the
   // workspace and are merged by the combine kernel
@@ -80,9 +83,11 @@ struct AttendArgs {
   int32_t parts_per_xcd;
   int32_t n_parts;
   float* ws_o;            // [n_parts][queries per workgroup][D] f32, sum p V
-  float* ws_ml;           // [n_parts][queries per workgroup][2] f32 (m, sum p)
+  float* ws_ml;           // [n_parts][queries per workgroup][4] f32 (m, sum p, sum p'^2, 0)
+  uint32_t* flags;        // [n_work] 1 = unit flagged as peaked, then [n_work] = flagged count
   // per-window key factors (written by the factors kernel of the same call):
-  float* fac_l;           // [n_kv_heads][ring tiles][64] float4 records (sk', log2(55 rho) / sk', 127 + e, 0)
+  float* fac_l;           // [n_kv_heads][ring tiles][64] float4 records (kf, log2(55 rho) / kf, 127 + e, 0),
+                          // kf = max(sk, 2^-60) log2(e) / sqrt(D)
   uint8_t* fac_u;         // [n_kv_heads][ring tiles][2][64] e4m3 rows of 2^-2 / rho
   int32_t n_kv_heads;
   int32_t ring_tiles;     // slots_padded / 64
@@ -129,8 +134,9 @@ __host__ __device__ inline int attend_window_tiles(const AttendArgs& a) {
 int attend_max_parts();
 // workspace of rtv_attend: split-key-range partials and the per-window key
 // factors; attend_set_workspace points the arguments into it
-size_t attend_workspace_bytes(int head_dim, int n_kv_heads, int64_t slots_padded);
-void attend_set_workspace(AttendArgs& a, void* ws, int head_dim, int n_kv_heads, int64_t slots_padded);
+size_t attend_workspace_bytes(int head_dim, int n_kv_heads, int64_t slots_padded, int64_t n_units);
+void attend_set_workspace(AttendArgs& a, void* ws, int head_dim, int n_kv_heads, int64_t slots_padded,
+                          int64_t n_units);
 hipError_t attend_capacity(int* workgroups);
 
 hipError_t launch_append(const AppendArgs& args, int head_dim, hipStream_t stream);

@@ -71,6 +71,13 @@ rtv_status check_config(const rtv_config* c) {
   return RTV_OK;
 }
 
+// units of attention work per call: query tiles x query heads
+int64_t attend_units(const rtv_config& c) {
+  const int64_t n = (int64_t)c.chunk_frames * c.tokens_per_frame;
+  const int64_t qpb = rtv::attend_queries_per_block();
+  return (n + qpb - 1) / qpb * c.n_q_heads;
+}
+
 rtv_status make_plan(const rtv_config* c, Plan* p) {
   rtv_status st = check_config(c);
   if (st != RTV_OK) return st;
@@ -84,8 +91,9 @@ rtv_status make_plan(const rtv_config* c, Plan* p) {
   if (!mul_ok(tmp, c->head_dim, &rope_elems)) return RTV_ERR_INVALID_ARG;   // (D/2) * 2 floats
   if (!mul_ok(rope_elems, 4, &tmp)) return RTV_ERR_INVALID_ARG;
   p->rope_bytes = align_up((size_t)tmp);
-  // attention workspace (partial results of split key ranges), shared by all layers
-  p->ws_bytes = align_up(rtv::attend_workspace_bytes(c->head_dim, c->n_kv_heads, Sp));
+  // attention workspace (partial results of split key ranges, key factors,
+  // peaked-unit flags), shared by all layers
+  p->ws_bytes = align_up(rtv::attend_workspace_bytes(c->head_dim, c->n_kv_heads, Sp, attend_units(*c)));
   // per-layer ring state for the device-state mode
   p->state_bytes = align_up((size_t)c->n_layers * sizeof(rtv::DevRingState));
   if (!mul_ok((int64_t)c->n_kv_heads * c->head_dim, Sp, &tmp)) return RTV_ERR_INVALID_ARG;
@@ -232,16 +240,20 @@ rtv_status rtv_cache_create(const rtv_config* cfg, void* dev_buf, size_t bytes, 
   }
 
   const int64_t npos = (int64_t)cfg->max_global_frames * cfg->tokens_per_frame;
+  const size_t table_floats = (size_t)npos * cfg->head_dim;
   std::vector<float> table;
-  try {
-    table.resize((size_t)npos * cfg->head_dim);
-  } catch (...) {
-    delete c;
-    return RTV_ERR_INVALID_ARG;
+  const float* src = cfg->rope_cos_sin_host;
+  if (!src) {
+    try {
+      table.resize(table_floats);
+    } catch (...) {
+      delete c;
+      return RTV_ERR_INVALID_ARG;
+    }
+    fill_rope(cfg->head_dim, cfg->rope_base, 0, npos, table.data());
+    src = table.data();
   }
-  fill_rope(cfg->head_dim, cfg->rope_base, 0, npos, table.data());
-  hipError_t e = hipMemcpyAsync(c->rope, table.data(), table.size() * sizeof(float),
-                                hipMemcpyHostToDevice, s);
+  hipError_t e = hipMemcpyAsync(c->rope, src, table_floats * sizeof(float), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipMemsetAsync(c->base + p.rope_bytes, 0, p.total - p.rope_bytes, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e == hipSuccess) e = rtv::attend_capacity(&c->capacity);
@@ -273,6 +285,20 @@ rtv_status rtv_cache_layout(const rtv_cache* c, int32_t layer, rtv_layout* out) 
   out->committed_frames = L.committed;
   out->appended = L.appended;
   out->reserved = 0;
+  return RTV_OK;
+}
+
+rtv_status rtv_cache_peaked_units(const rtv_cache* c, int32_t* units, void* stream) {
+  if (!c || !units) return RTV_ERR_INVALID_ARG;
+  rtv::AttendArgs a;
+  rtv::attend_set_workspace(a, c->ws, c->cfg.head_dim, c->cfg.n_kv_heads, c->plan.slots_padded,
+                            attend_units(c->cfg));
+  uint32_t n = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&n, a.flags + attend_units(c->cfg), sizeof(n), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return RTV_ERR_HIP;
+  *units = (int32_t)n;
   return RTV_OK;
 }
 
@@ -400,7 +426,9 @@ rtv_status rtv_attend(rtv_cache* c, int32_t layer, const void* q_bf16, int64_t q
   a.capacity = c->capacity;
   a.two_term_q = cfg.query_terms == 2;
   a.two_term_p = cfg.prob_terms == 2;
-  rtv::attend_set_workspace(a, c->ws, cfg.head_dim, cfg.n_kv_heads, c->plan.slots_padded);
+  a.check_peaked = cfg.prob_terms == 0;
+  a.redo = 0;
+  rtv::attend_set_workspace(a, c->ws, cfg.head_dim, cfg.n_kv_heads, c->plan.slots_padded, attend_units(cfg));
   if (rtv::launch_attend(a, cfg.head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
     return RTV_ERR_HIP;
   return RTV_OK;
