@@ -115,6 +115,14 @@ __device__ __forceinline__ v16f mfma_fp8(const v8i& a, const v8i& b, const v16f&
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4f mfma16_fp8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma16_fp8_bscaled(const v8i& a, const v8i& b, const v4f& c, int e) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, e);
+}
+
 // the same with the B operand scaled by 2^(e - 127) (E8M0 exponent e):
 // adds the low-order e4m3 part of a two-term operand
 __device__ __forceinline__ v16f mfma_fp8_bscaled(const v8i& a, const v8i& b, const v16f& c, int e) {
@@ -527,9 +535,12 @@ __device__ __forceinline__ int query_exp(float amax) {
   return e < -120 ? -120 : (e > 120 ? 120 : e);
 }
 
-// G of query li of the lane (PV layout): the diagonal element (li, li) of the
-// 32x32 product P' P'^T sits in lane 32 ((li >> 2) & 1) + li, register
-// 4 (li >> 3) + (li & 3); both lanes of the query receive it.
+// Peaked-row statistic: G = sum_k P'_k^2 of each query, the diagonal of the
+// 32x32 product P' P'^T of the wave's P' codes with themselves (the A and B
+// operand layouts of v_mfma_f32_32x32x64 agree: lane (hh, li) holds row /
+// column li and the keys of half hh).  Diagonal element (li, li) sits in lane
+// 32 ((li >> 2) & 1) + li, register 4 (li >> 3) + (li & 3); both lanes of the
+// query (li and li + 32) receive it.
 __device__ __forceinline__ float gram_diag(const v16f& g, int li, int hh) {
   const int gi = 4 * (li >> 3) + (li & 3);
   float x = 0.0f;
@@ -959,13 +970,6 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend_kernel(
 // query block; its rare updates reduce over the four lanes of a query.
 __device__ __forceinline__ int key16(int kb, int r) { return vt_key(16 * (r >> 2) + 4 * kb + (r & 3)); }
 
-typedef float v4f __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ v4f mfma16_fp8(const v8i& a, const v8i& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-__device__ __forceinline__ v4f mfma16_fp8_bscaled(const v8i& a, const v8i& b, const v4f& c, int e) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, e);
-}
 // max over the four lanes i, i + 16, i + 32, i + 48 (the lanes of one query)
 __device__ __forceinline__ float quad_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -1482,7 +1486,7 @@ hipError_t launch_attend_d(const AttendArgs& args_in, hipStream_t stream) {
       keys += args.seg_hi[s] - args.seg_lo[s];
     }
     n_tiles = attend_window_tiles(args);
-    short_window = keys < kPreciseKeys || args.two_term_p;
+    short_window = keys < kPreciseKeys;
     attend_schedule(args, n_tiles, kMaxParts);
     grid_per_xcd = args.full_per_xcd + args.parts_per_xcd;
     rem = args.n_work - args.n_full;
@@ -1490,13 +1494,14 @@ hipError_t launch_attend_d(const AttendArgs& args_in, hipStream_t stream) {
     // Device-state mode: the kernels derive the window and the schedule, so
     // the variant and the grids are fixed by the ring's shape.  Every window
     // holds at least one chunk and starts on a chunk boundary when the cap
-    // is a multiple of the chunk; the grids cover the largest window.  The
-    // variant follows the shortest window (one chunk): a ring whose chunk is
-    // under 8192 keys takes the two-term kernel on every window.
+    // is a multiple of the chunk; the grids cover the largest window.  With
+    // unchecked one-code weights the variant follows the shortest window (one
+    // chunk): a ring whose chunk is under 8192 keys takes the two-term kernel
+    // on every window.
     const RingShape& sh = args.shape;
     const int64_t chunk = (int64_t)sh.chunk_frames * sh.tokens_per_frame;
     aligned = chunk % 64 == 0 && sh.max_window_frames % sh.chunk_frames == 0;
-    short_window = chunk < kPreciseKeys || args.two_term_p;
+    short_window = chunk < kPreciseKeys;
     n_tiles = (int)(((int64_t)sh.capacity_frames * sh.tokens_per_frame + 63) / 64) + 1;
     AttendArgs whole = args, most = args;
     attend_schedule(whole, 1, kMaxParts);
@@ -1505,8 +1510,12 @@ hipError_t launch_attend_d(const AttendArgs& args_in, hipStream_t stream) {
     grid_per_xcd = g1 > g2 ? g1 : g2;
     rem = most.n_work - most.n_full;
   }
-  const bool two_term_q = short_window || args.two_term_q;
-  const bool check = !short_window && args.check_peaked;
+  // prob_terms 2: two terms everywhere; 0 (checked): the one-code kernel and
+  // its check on every window, in both modes alike (short windows are usually
+  // flagged and recomputed); 1 (unchecked): two terms below 8192 keys
+  const bool check = args.check_peaked && !args.two_term_p;
+  const bool precise = args.two_term_p || (!check && short_window);
+  const bool two_term_q = precise || args.two_term_q;
   args.check_peaked = check ? 1 : 0;
   args.redo = 0;
   {
@@ -1515,9 +1524,9 @@ hipError_t launch_attend_d(const AttendArgs& args_in, hipStream_t stream) {
   }
   const dim3 g(8 * grid_per_xcd), b(kThreads);
   if (aligned)
-    launch_variant<D, false>(short_window, two_term_q, check, g, b, args, stream);
+    launch_variant<D, false>(precise, two_term_q, check, g, b, args, stream);
   else
-    launch_variant<D, true>(short_window, two_term_q, check, g, b, args, stream);
+    launch_variant<D, true>(precise, two_term_q, check, g, b, args, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 cg(rem, kQPB / kCombineQ), cb(kCombineQ * kCombineT);

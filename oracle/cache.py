@@ -40,7 +40,10 @@ class ChunkEntry:
 
 class OracleKVCache:
     def __init__(self, n_layers, n_kv_heads, head_dim, tokens_per_frame,
-                 chunk_frames, capacity_frames, rope_base=10000.0):
+                 chunk_frames, capacity_frames, rope_base=10000.0, rope_table=None):
+        """rope_table: optional float32 [positions, D/2, 2] (cos, sin) table to
+        use instead of evaluating rope.cos_sin_table, so that a test can hand
+        one table to both implementations."""
         if capacity_frames % chunk_frames:
             raise ValueError("capacity_frames must be a multiple of chunk_frames")
         self.n_layers = n_layers
@@ -55,13 +58,18 @@ class OracleKVCache:
         self.next_global_frame = [0] * n_layers
         self.committed = [0] * n_layers
         self._table_cache = {}
+        self.rope_table = None if rope_table is None else np.asarray(rope_table, dtype=np.float32)
 
     # -- RoPE table of the chunk at a global frame ---------------------------
     def chunk_table(self, global_frame):
         key = global_frame
         if key not in self._table_cache:
             pos = rope.chunk_positions(global_frame, self.F, self.T)
-            self._table_cache = {key: rope.cos_sin_table(pos, self.head_dim, self.base)}
+            if self.rope_table is not None:
+                rows = self.rope_table[pos]
+                self._table_cache = {key: (rows[:, :, 0].copy(), rows[:, :, 1].copy())}
+            else:
+                self._table_cache = {key: rope.cos_sin_table(pos, self.head_dim, self.base)}
         return self._table_cache[key]
 
     # -- cache upkeep --------------------------------------------------------

@@ -8,10 +8,13 @@ step after step with new inputs.  Every replay is checked against an eager
 host-state run of the same inputs, with eager work and synchronizations
 between the replays.
 """
+import numpy as np
 import pytest
 import torch
 
-from tests.gpu_helpers import to_dev_bf16
+from oracle.cache import OracleKVCache
+from tests.attention_check import check_attention
+from tests.gpu_helpers import bf16_to_np_f32, to_dev_bf16
 from workloads import get_workload, qkv_normal
 
 pytestmark = pytest.mark.gpu
@@ -69,12 +72,17 @@ def test_device_state_eager_equals_host_state(rtv_lib):
         assert (lh.next_global_frame, lh.committed_frames) == (ld.next_global_frame, ld.committed_frames)
 
 
-def _graph_replay_case(rtv_lib, wl, n_layers, steps, capture_at, maxw=0):
+def _graph_replay_case(rtv_lib, wl, n_layers, steps, capture_at, maxw=0, oracle_rows=None):
     """Eager device-state steps up to capture_at, one step captured, then
     replays with each step's inputs copied into the captured buffers; each
-    step compared with an eager host-state cache fed the same inputs."""
+    step compared with an eager host-state cache fed the same inputs and, on
+    `oracle_rows` (query rows of every head), with the oracle."""
     cfg = _cfg(rtv_lib, wl, n_layers, (steps + 2) * wl.chunk_frames)
     host, dev = rtv_lib.RtvCache(cfg), rtv_lib.RtvCache(cfg)
+    ora = None
+    if oracle_rows is not None:
+        ora = OracleKVCache(n_layers, wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame, wl.chunk_frames,
+                            wl.capacity_frames, wl.rope_base)
     bufs = [tuple(t.clone() for t in qkv) for qkv in _inputs(wl, n_layers, 0, 0)]
     outs = [torch.empty_like(q) for q, _, _ in bufs]
 
@@ -113,6 +121,13 @@ def _graph_replay_case(rtv_lib, wl, n_layers, steps, capture_at, maxw=0):
         for layer in range(n_layers):
             assert _same(outs[layer], want[layer]), (step, layer)
         assert _same_rings(host, dev, n_layers), step
+        if ora is not None:
+            for layer, (q, k, v) in enumerate(qkv_normal(wl, layer, step, 0) for layer in range(n_layers)):
+                ora.append(layer, k, v)
+                ref = ora.attend(layer, q, max_window_frames=maxw, rows=oracle_rows)
+                check_attention(bf16_to_np_f32(outs[layer])[oracle_rows], ref,
+                                f"graph replay step={step} layer={layer} window={ora.window_frames(layer, maxw)}")
+                ora.advance(layer)
         host.advance(-1)
     dev.device_state_end()
     for layer in range(n_layers):
@@ -135,9 +150,12 @@ def test_graph_replay_tiny_capped_window(rtv_lib):
 def test_graph_replay_layer_shape(rtv_lib):
     """12 heads x 128, 16-frame ring: captured at the first step, replayed while
     the window grows 4 -> 16 frames and once more in steady state (47872 keys,
-    split tail and combine)."""
+    split tail and combine); every replay also against the oracle on 64
+    sampled query rows of every head."""
     wl = get_workload("layer")
-    _graph_replay_case(rtv_lib, wl, n_layers=1, steps=6, capture_at=0)
+    rows = np.unique(np.concatenate([[0, wl.chunk_tokens - 1],
+                                     np.random.default_rng(8).choice(wl.chunk_tokens, 64, replace=False)]))
+    _graph_replay_case(rtv_lib, wl, n_layers=1, steps=6, capture_at=0, oracle_rows=rows)
 
 
 def test_device_state_rope_exhaustion(rtv_lib):
