@@ -3,6 +3,7 @@ import numpy as np
 import torch
 
 from oracle import bf16, e4m3, gemm
+from tests.gemm_model import grouped_truncation_sum as _grouped_truncation_sum
 
 
 def test_bf16_rounding_matches_torch_on_float32_inputs():
@@ -66,30 +67,6 @@ def test_fp32_accumulation_within_bound():
     assert np.all(np.abs(acc - exact) <= gemm.error_bound(xc, sx, wc, sw) + 1e-30)
 
 
-def _grouped_truncation_sum(a_codes, b_codes, group=8, align_bits=13):
-    """Plain model of an FP8 dot product that aligns each group of `group`
-    consecutive products to the group's largest exponent sum and truncates
-    them toward zero to 2^(E - align_bits), then adds the groups exactly."""
-    ea = gemm.code_exponents(a_codes)
-    eb = gemm.code_exponents(b_codes)
-    a = e4m3.decode(a_codes)
-    b = e4m3.decode(b_codes)
-    M, K = a.shape
-    N = b.shape[1]
-    out = np.zeros((M, N))
-    for m in range(M):
-        for n in range(N):
-            for g0 in range(0, K, group):
-                sl = slice(g0, g0 + group)
-                esum = ea[m, sl] + eb[sl, n]
-                if np.all(np.isneginf(esum)):
-                    continue
-                lsb = 2.0 ** (np.max(esum) - align_bits)
-                p = a[m, sl] * b[sl, n]
-                out[m, n] += np.sum(np.trunc(p / lsb) * lsb)
-    return out
-
-
 def test_code_exponents():
     assert gemm.code_exponents(np.array([0x38]))[0] == 0         # 1.0
     assert gemm.code_exponents(np.array([0x7E]))[0] == 8         # 448
@@ -142,3 +119,58 @@ def test_group_truncation_model_reproduces_cancellation_cases():
     assert _grouped_truncation_sum(a, b)[0, 0] == 0.09375
     a[0, 2], a[0, 9] = 0, c[0]
     assert _grouped_truncation_sum(a, b)[0, 0] == 0.109375
+
+
+def _designed_group_losses():
+    """Rows whose every group holds one product of exponent 8 (448 x 1) and
+    seven just below the alignment step 2^(8-13): 0.029296875 = 2^-6 x 1.875,
+    each of which the grouped truncation drops whole, and its negation."""
+    small = 0x0F                                       # 2^-6 * (1 + 7/8)
+    a = np.full((2, 64), small, np.uint8)
+    a[:, ::8] = 0x7E                                   # 448 leads each group
+    a[1] |= 0x80                                       # the negated row
+    b = np.full((64, 1), 0x38, np.uint8)               # 1.0
+    return a, b
+
+
+def _worst_ratio(a, b, align_bits):
+    exact = gemm.gemm_fp64(a, 1.0, b, 1.0)
+    model = _grouped_truncation_sum(a, b)
+    bound = gemm.error_bound(a, 1.0, b, 1.0, align_bits=align_bits)
+    return float(np.max(np.abs(model - exact) / bound))
+
+
+def test_group_term_is_tight_on_designed_losses():
+    """The bound is not loose: on the designed rows the model's error reaches
+    0.82 of it (7 of the 8 alignment steps of each group), and a bound built
+    with a coarser alignment (align_bits <= 10) would stay under a quarter."""
+    a, b = _designed_group_losses()
+    r = _worst_ratio(a, b, 13)
+    print(f"designed groups: error / bound = {r:.3f}")
+    assert 0.25 <= r <= 1.0
+    assert r > 0.8
+    for bits in (10, 9, 8):
+        assert _worst_ratio(a, b, bits) < 0.25, bits
+    # the float32-only bound misses these losses by far
+    exact = gemm.gemm_fp64(a, 1.0, b, 1.0)
+    f32_only = 64 * 2.0 ** -24 * (np.abs(e4m3.decode(a)) @ np.abs(e4m3.decode(b)))
+    assert np.all(np.abs(_grouped_truncation_sum(a, b) - exact) > 100 * f32_only)
+
+
+def test_group_term_on_full_range_codes():
+    """Random full-range codes (products over 35 binades): the model's error
+    exceeds the float32-only bound on some outputs and stays within the group
+    bound everywhere; its worst ratio to the bound (about 0.06: random groups
+    rarely lose all eight steps, and the bound takes the group's largest
+    exponents of A and B separately) is printed."""
+    rng = np.random.default_rng(31)
+    a = rng.integers(0, 256, (16, 128), dtype=np.uint8)
+    b = rng.integers(0, 256, (128, 8), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x7E
+    b[(b & 0x7F) == 0x7F] = 0x7E
+    r = _worst_ratio(a, b, 13)
+    print(f"full-range codes: worst error / bound = {r:.3f}")
+    assert r <= 1.0
+    exact = gemm.gemm_fp64(a, 1.0, b, 1.0)
+    f32_only = 128 * 2.0 ** -24 * (np.abs(e4m3.decode(a)) @ np.abs(e4m3.decode(b)))
+    assert np.any(np.abs(_grouped_truncation_sum(a, b) - exact) > f32_only)
