@@ -277,6 +277,19 @@ size_t rtv_quant_workspace_bytes(int64_t n);
 rtv_status rtv_quant_fp8_per_tensor(const void* x_bf16, int64_t n, uint8_t* codes_dev,
                                     float* scale_dev, void* workspace, void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the quantization
+ * above with its workspace held by the library, a static device array of 1024
+ * words per GPU (4 KiB, kept until the process ends; the first call on a
+ * device looks up that device's copy).  Same results as
+ * rtv_quant_fp8_per_tensor for every n >= 0: a launch uses at most 1024
+ * partial maxima whatever n is, so no input is too large for the array.
+ * Allocates nothing.  Calls that may overlap on one GPU race on the array:
+ * order them (e.g. one stream).  Errors: INVALID_ARG (pointers, alignment,
+ * n < 0), HIP (the array's address could not be found). */
+rtv_status rtv_quant_fp8_per_tensor_static(const void* x_bf16, int64_t n, uint8_t* codes_dev,
+                                           float* scale_dev, void* stream);
+
 /* C[M][N] (bf16, row stride ldc) = (*sa) * (*sb) * A[M][K] * B[K][N], A and B
  * e4m3 codes, A row-major [M][K], B given TRANSPOSED as Bt[N][K] (row-major),
  * f32 accumulation, one rounding to bf16.  K must be a multiple of 64, M and N

@@ -101,6 +101,7 @@ def _load():
         "rtv_status_string": (ctypes.c_char_p, [I32]),
         "rtv_quant_workspace_bytes": (SZ, [I64]),
         "rtv_quant_fp8_per_tensor": (I32, [P, I64, P, P, P, P]),
+        "rtv_quant_fp8_per_tensor_static": (I32, [P, I64, P, P, P]),
         "rtv_gemm_fp8": (I32, [P, P, P, P, P, I32, I32, I32, I64, P]),
         "rtv_qkv_gemm_append": (I32, [P, I32, P, P, P, P, I32, I32, I32, P, I64, P]),
     }
@@ -123,7 +124,8 @@ EXPORTED = (
     "rtv_attend", "rtv_advance", "rtv_device_state_begin", "rtv_device_state_end", "rtv_cache_layout",
     "rtv_cache_window", "rtv_cache_peaked_units", "rtv_ring_window",
     "rtv_rope_fill_host", "rtv_encode_e4m3", "rtv_status_string",
-    "rtv_quant_workspace_bytes", "rtv_quant_fp8_per_tensor", "rtv_gemm_fp8", "rtv_qkv_gemm_append",
+    "rtv_quant_workspace_bytes", "rtv_quant_fp8_per_tensor", "rtv_quant_fp8_per_tensor_static", "rtv_gemm_fp8",
+    "rtv_qkv_gemm_append",
 )
 
 
@@ -222,6 +224,11 @@ def rtv_quant_workspace_bytes(n) -> int:
 def rtv_quant_fp8_per_tensor(x_ptr, n, codes_ptr, scale_ptr, ws_ptr, stream):
     check(lib.rtv_quant_fp8_per_tensor(x_ptr, n, codes_ptr, scale_ptr, ws_ptr, stream),
           "rtv_quant_fp8_per_tensor")
+
+
+def rtv_quant_fp8_per_tensor_static(x_ptr, n, codes_ptr, scale_ptr, stream):
+    check(lib.rtv_quant_fp8_per_tensor_static(x_ptr, n, codes_ptr, scale_ptr, stream),
+          "rtv_quant_fp8_per_tensor_static")
 
 
 def rtv_gemm_fp8(a_ptr, sa_ptr, bt_ptr, sb_ptr, c_ptr, M, N, K, ldc, stream):

@@ -36,6 +36,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <mutex>
 
 namespace rtv {
 namespace {
@@ -433,14 +434,56 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
 
 int quant_max_partials() { return 1024; }
 
+static int quant_blocks(int64_t n) {
+  const int64_t per_block = (int64_t)kQuantThreads * 8 * 4;
+  return (int)std::min<int64_t>(quant_max_partials(), std::max<int64_t>(1, (n + per_block - 1) / per_block));
+}
+
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, uint8_t* codes, float* scale,
                             uint32_t* partial, hipStream_t stream) {
-  const int64_t per_block = (int64_t)kQuantThreads * 8 * 4;
-  const int blocks = (int)std::min<int64_t>(quant_max_partials(), std::max<int64_t>(1, (n + per_block - 1) / per_block));
+  const int blocks = quant_blocks(n);
   hipLaunchKernelGGL(quant_amax_kernel, dim3(blocks), dim3(kQuantThreads), 0, stream, x, n, partial);
   hipLaunchKernelGGL(quant_apply_kernel, dim3(blocks), dim3(kQuantThreads), 0, stream, x, n,
                      (const uint32_t*)partial, blocks, codes, scale);
   return hipGetLastError();
+}
+
+// Workspace of the per-tensor quantization held by the library itself, for
+// callers that cannot allocate: one block's max |x| per word.  Every call
+// writes the words it reads, so nothing needs clearing; calls that overlap on
+// one GPU share the array and race.  Each GPU holds its own copy; host code
+// reaches it only through the address hipGetSymbolAddress gives per device.
+constexpr int kQuantScratchWords = 1024;
+static __device__ __align__(256) uint32_t scratch[kQuantScratchWords];
+
+static hipError_t quant_scratch(uint32_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex lock;
+  static uint32_t* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(lock);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
+
+int quant_scratch_words() { return kQuantScratchWords; }
+
+hipError_t launch_quant_fp8_static(const uint16_t* x, int64_t n, uint8_t* codes, float* scale,
+                                   hipStream_t stream) {
+  if (quant_blocks(n) > kQuantScratchWords) return hipErrorInvalidValue;
+  uint32_t* partial = nullptr;
+  const hipError_t e = quant_scratch(&partial);
+  if (e != hipSuccess) return e;
+  return launch_quant_fp8(x, n, codes, scale, partial, stream);
 }
 
 static GemmArgs gemm_args(const uint8_t* a, const float* sa, const uint8_t* bt, const float* sb, uint16_t* c,

@@ -148,6 +148,10 @@ int attend_queries_per_block();
 int quant_max_partials();
 hipError_t launch_quant_fp8(const uint16_t* x, int64_t n, uint8_t* codes, float* scale,
                             uint32_t* partial, hipStream_t stream);
+// the same with the partials in the library's static device array (no allocation)
+hipError_t launch_quant_fp8_static(const uint16_t* x, int64_t n, uint8_t* codes, float* scale,
+                                   hipStream_t stream);
+int quant_scratch_words();
 // FP8 QKV GEMM whose epilogue writes Q as bf16 and K, V (RoPE on K, e4m3 per
 // (token, head)) straight into the ring slots of the chunk
 struct QkvAppendArgs {

@@ -558,6 +558,18 @@ rtv_status rtv_quant_fp8_per_tensor(const void* x_bf16, int64_t n, uint8_t* code
   return RTV_OK;
 }
 
+rtv_status rtv_quant_fp8_per_tensor_static(const void* x_bf16, int64_t n, uint8_t* codes_dev,
+                                           float* scale_dev, void* stream) {
+  if (n < 0 || !scale_dev || (n > 0 && (!x_bf16 || !codes_dev))) return RTV_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(x_bf16) % 16 || reinterpret_cast<uintptr_t>(codes_dev) % 8 ||
+      reinterpret_cast<uintptr_t>(scale_dev) % 4)
+    return RTV_ERR_INVALID_ARG;
+  if (rtv::launch_quant_fp8_static(static_cast<const uint16_t*>(x_bf16), n, codes_dev, scale_dev,
+                                   static_cast<hipStream_t>(stream)) != hipSuccess)
+    return RTV_ERR_HIP;
+  return RTV_OK;
+}
+
 rtv_status rtv_gemm_fp8(const uint8_t* a, const float* sa_dev, const uint8_t* bt,
                         const float* sb_dev, void* c_bf16, int32_t M, int32_t N, int32_t K,
                         int64_t ldc, void* stream) {
