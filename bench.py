@@ -36,6 +36,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak, TFLOP/s
+# the step's attention kernels: the one-code kernel with the peaked-row check,
+# and the two-term kernel that recomputes flagged query tiles
+ATTEND_KERNEL = "attend16_kernel<false, false, false, true>"
+REDO_KERNEL = "attend16_kernel<false, true, true, false>"
 
 
 def parse():
@@ -46,6 +50,10 @@ def parse():
     p.add_argument("--layers", type=int, default=60)
     p.add_argument("--calls", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the other workloads' figures (stress ring, GQA, projection) in the default line")
+    p.add_argument("--config-steps", type=int, default=3,
+                   help="timed calls per figure of the other workloads in the default line")
     p.add_argument("--eager", action="store_true",
                    help="time eagerly launched steps (default: replays of one captured HIP graph per step)")
     p.add_argument("--workload", choices=["step", "projection", "attention"], default="step",
@@ -218,8 +226,13 @@ def cpu_baseline(wl, heads: int):
     t_attend = t_heads * wl.n_q_heads / heads
     calls = wl.n_layers * wl.calls_per_layer
     step_ms = (t_append + t_attend) * calls * 1e3
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = None
     return {
         "value": round(step_ms, 1), "unit": "ms/step", "cores": int(blas_threads), "kind": "oracle",
+        "cpu_count": os.cpu_count(), "affinity_cpus": affinity,
         "sample": (f"one call measured: oracle RoPE+e4m3 upkeep of the {n}-token chunk x {wl.n_kv_heads} "
                    f"heads ({t_append:.2f} s) and float64 attention of all {n} query rows of {heads} of "
                    f"{wl.n_q_heads} heads over {C * T} keys ({t_heads:.2f} s); scaled to {wl.n_q_heads} heads "
@@ -308,18 +321,23 @@ def projection(args):
         "gemm_frac_fp8_peak": round(flops / (t_gemm * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
         "fused_frac_fp8_peak": round(flops / (t_fused * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
     }
-    print(json.dumps(result), flush=True)
+    del cache, x, wt, xc, wc, qkv, q_out, ws
+    return result
 
 
 def attention_configs(args):
-    """One attention call at the two other configurations the hot path is
-    measured on:
+    """One attention call at the other configurations the hot path is
+    measured on, with the library's default attention weights (one code,
+    checked for peaked rows):
     - the stress ring: K/V Student-t (nu = 3) with 4 x20 outlier channels per
-      head and 1 % zero rows (the seeded host generator), two-term queries, a
-      24-frame ring read at every window length of its cycle, 4..24 frames;
+      head and 1 % zero rows (the seeded host generator), a 24-frame ring read
+      at every window length of its cycle, 4..24 frames (its rows are peaked:
+      every query tile is recomputed with two-term queries and weights);
     - the projection workload's attention: 24 query heads over 12 KV heads
       (GQA 2:1) at the full 32-frame ring, 95744 keys (inputs N(0,1) drawn on
-      the device).
+      the device);
+    - the step's layer shape at the full window with each choice of weights
+      (0: checked one code, the default; 1: one code unchecked; 2: two terms).
     Each call is timed between HIP events over `steps` calls after `warmup`."""
     import torch
 
@@ -352,7 +370,7 @@ def attention_configs(args):
     wl = get_workload("stress")
     fills = wl.capacity_frames // wl.chunk_frames
     cfg = rtv.RtvConfig(1, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.tokens_per_frame, wl.chunk_frames,
-                        wl.capacity_frames, (fills + 2) * wl.chunk_frames, wl.rope_base, query_terms=2)
+                        wl.capacity_frames, (fills + 2) * wl.chunk_frames, wl.rope_base)
     cache = rtv.RtvCache(cfg, device=dev)
     def bits_to_dev(bits):
         return torch.from_numpy(bits.view("int16")).view(torch.bfloat16).to(dev)
@@ -367,7 +385,7 @@ def attention_configs(args):
     stress = []
     for frames in wl.window_cycle:
         ms = timed(lambda: cache.attend(0, q, out, max_window_frames=frames, stream=stream))
-        stress.append(entry(wl, frames, ms))
+        stress.append(dict(entry(wl, frames, ms), recomputed_units=cache.peaked_units()))
     del cache, q, out
 
     # the projection workload's GQA attention over the full ring
@@ -384,15 +402,17 @@ def attention_configs(args):
     q = device_normal_bf16((wp.chunk_tokens, wp.n_q_heads, wp.head_dim), (6, 0, 0), dev)
     out = torch.empty_like(q)
     gqa = entry(wp, wp.capacity_frames, timed(lambda: cache.attend(0, q, out, stream=stream)))
+    gqa["recomputed_units"] = cache.peaked_units()
     del cache, q, out
 
     # the step's layer shape at the full window, with one-code (default) and
-    # two-term attention weights (prob_terms = 2, the choice for peaked rows)
+    # each choice of attention weights (0: one code checked for peaked rows,
+    # the default; 1: one code unchecked; 2: two terms everywhere)
     ws = get_workload("step")
     fills = ws.capacity_frames // ws.chunk_frames
     kv_shape = (ws.chunk_tokens, ws.n_kv_heads, ws.head_dim)
     weights = {}
-    for terms in (1, 2):
+    for terms in (0, 1, 2):
         cfg = rtv.RtvConfig(1, ws.n_q_heads, ws.n_kv_heads, ws.head_dim, ws.tokens_per_frame, ws.chunk_frames,
                             ws.capacity_frames, (fills + 2) * ws.chunk_frames, ws.rope_base, prob_terms=terms)
         cache = rtv.RtvCache(cfg, device=dev)
@@ -405,20 +425,21 @@ def attention_configs(args):
         out = torch.empty_like(q)
         weights[f"prob_terms_{terms}"] = entry(ws, ws.capacity_frames,
                                                timed(lambda: cache.attend(0, q, out, stream=stream)))
+        weights[f"prob_terms_{terms}"]["recomputed_units"] = cache.peaked_units()
         del cache, q, out
     result = {
         "metric": "ms per attention call at the stress ring (every window length) and the GQA workload",
         "value": gqa["ms"], "unit": "ms", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
         "dtype": "fp8-e4m3 (f32 accumulate)", "data": "synthetic",
         "config": {"workload": (f"stress: {wl.n_q_heads} heads x {wl.head_dim}, {wl.chunk_tokens}-token chunk, "
-                                f"Student-t K/V with outlier channels and zero rows, two-term queries, "
+                                f"Student-t K/V with outlier channels and zero rows, "
                                 f"{wl.capacity_frames}-frame ring, windows {list(wl.window_cycle)} frames; "
                                 f"gqa: {wp.n_q_heads} query heads over {wp.n_kv_heads} KV heads, "
                                 f"{wp.capacity_frames}-frame ring; layer: the step's layer shape at "
-                                f"{ws.capacity_frames} frames, prob_terms 1 and 2")},
+                                f"{ws.capacity_frames} frames, prob_terms 0, 1 and 2")},
         "stress": stress, "gqa": gqa, "layer_full_window": weights,
     }
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def main():
@@ -427,13 +448,13 @@ def main():
         if args.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)
             sys.exit(2)
-        attention_configs(args)
+        print(json.dumps(attention_configs(args)), flush=True)
         return
     if args.workload == "projection":
         if args.gpus != 1:
             print("bench.py runs on one GPU only", file=sys.stderr)
             sys.exit(2)
-        projection(args)
+        print(json.dumps(projection(args)), flush=True)
         return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_bytes, args.traffic_json)
@@ -582,14 +603,15 @@ def main():
 
     # HBM bytes per rtv_attend call (attention + combine kernels of the
     # steady-state window) and per append, from the calibrated counters
-    att_traffic = traffic_of(args.traffic_json, "attend16_kernel<false, false, false>")
+    att_traffic = traffic_of(args.traffic_json, ATTEND_KERNEL)
     comb_traffic = traffic_of(args.traffic_json, "combine_kernel<128>")
     fac_traffic = traffic_of(args.traffic_json, "factors_kernel")
+    redo_traffic = traffic_of(args.traffic_json, REDO_KERNEL)
     app_traffic = traffic_of(args.traffic_json, "append_rope_quant_kernel<128")
     traffic = None
     if att_traffic:
         traffic = sum(v["bytes"] for v in att_traffic.values())
-        for extra in (comb_traffic, fac_traffic):
+        for extra in (comb_traffic, fac_traffic, redo_traffic):
             if extra:
                 traffic += sum(v["bytes"] for v in extra.values())
     app_bytes_measured = sum(v["bytes"] for v in app_traffic.values()) if app_traffic else None
@@ -621,8 +643,9 @@ def main():
         "tokens_appended_per_s": round(wl.calls_per_layer * wl.n_layers * n / (ms_per_step * 1e-3)),
         "roofline": {
             "bound": "mfma",
-            "kernel": ("rtv_attend = factors_kernel + attend16_kernel<false, false, false> + "
-                       "combine_kernel<128>"),
+            "kernel": (f"rtv_attend = factors_kernel<128> + {ATTEND_KERNEL} + combine_kernel<128> "
+                       f"(+ {REDO_KERNEL} and a second combine_kernel<128>, which recompute the query "
+                       f"tiles flagged as peaked and exit at once when none is)"),
             "achieved": round(att_tflops, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
             "avg_launch_ms": round(att_avg_ms, 4),
@@ -635,6 +658,7 @@ def main():
             "bytes_per_launch": app_bytes, "traffic": app_bytes_measured,
         },
         "wall_s_timed": round(wall, 3),
+        "recomputed_units_last_call": cache.peaked_units(stream=stream),
     }
     if args.copy_calibration:
         nb = args.copy_calibration << 20
@@ -644,6 +668,23 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = nb
+    if not args.no_configs:
+        # the other workloads' figures, in the same line (parity-test cases,
+        # not the headline): the stress ring at every window length, the GQA
+        # attention over 95744 keys, the layer shape with each weight choice,
+        # and the projection chunk
+        del inputs, out
+        cache.close()
+        del cache
+        torch.cuda.empty_cache()
+        sub = argparse.Namespace(**vars(args))
+        sub.steps, sub.warmup = args.config_steps, 1
+        att = attention_configs(sub)
+        result["configs"] = {"stress_ring": att["stress"], "gqa_95744_keys": att["gqa"],
+                             "layer_full_window_by_weights": att["layer_full_window"],
+                             "projection_chunk": {k: v for k, v in projection(sub).items()
+                                                  if k not in ("metric", "value", "unit", "higher_is_better",
+                                                               "steps", "warmup", "data")}}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads)
     print(json.dumps(result), flush=True)

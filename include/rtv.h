@@ -61,16 +61,16 @@ typedef struct rtv_config {
   int32_t chunk_frames;      /* F: frames appended per call (4 on the pages) */
   int32_t capacity_frames;   /* C: ring capacity in frames; multiple of F */
   int32_t max_global_frames; /* frames the session may ever append: extent of the RoPE table */
-  int32_t query_terms;       /* e4m3 terms carrying each query through the matrix cores:
+  int32_t query_terms;       /* e4m3 terms carrying each query through the matrix cores
+                              * (each query with its own power-of-two scale, applied
+                              * exactly by the matrix core):
                               * 1 (or 0): one term, relative rounding error 2^-4;
-                              * 2: hi + 2^-4 lo, relative error about 2^-8, for keys with
-                              * outlier channels or heavy tails, whose scores spread over
-                              * many binades and magnify the query's rounding (costs about
-                              * 20% more attention time on long windows).  Windows shorter
-                              * than 8192 keys always use two terms for queries and
-                              * probabilities. */
+                              * 2: hi + 2^-4 lo, relative error about 2^-8, on every window
+                              * (costs about 20% more attention time on long windows).
+                              * Query tiles recomputed as peaked (prob_terms 0) and the
+                              * two-term kernels always carry two terms. */
   int32_t prob_terms;        /* e4m3 terms carrying each attention weight P' into the PV
-                              * product on windows of 8192 keys or more:
+                              * product:
                               * 0 (default): one code read off the log domain (within one
                               * code step of the correctly rounded value, up to about 6%
                               * per weight), checked: every query row also measures how
@@ -82,12 +82,14 @@ typedef struct rtv_config {
                               * one-code errors average out, cost one extra matrix-core
                               * product per tile; each recomputed query tile costs about
                               * twice its one-code time;
-                              * 1: one code, unchecked: outside the attention tolerance on
-                              * peaked rows (a few keys carrying much of the weight);
+                              * 1: one code, unchecked, on windows of 8192 keys or more
+                              * (two terms on shorter ones; in the device-state mode the
+                              * choice follows the chunk length): outside the attention
+                              * tolerance on peaked rows (a few keys carrying much of the
+                              * weight);
                               * 2: two terms on every window, for callers that know their
-                              * attention is peaked (the configuration of windows under
-                              * 8192 keys, which always take it; about 1.9 times the
-                              * one-code time on a 47872-key window). */
+                              * attention is peaked (about 1.9 times the one-code time on
+                              * a 47872-key window). */
   double rope_base;          /* RoPE base (10000) */
   const float* rope_cos_sin_host;
                              /* optional host table [max_global_frames*T][D/2][2] of the
@@ -217,10 +219,10 @@ rtv_status rtv_advance(rtv_cache* cache, int32_t layer, void* stream);
  *   - rtv_advance enqueues a kernel that moves it;
  * so a sequence of these calls captured once (hipStreamBeginCapture, or
  * torch.cuda.graph) replays correctly step after step.  The results equal
- * the host-state calls' (same kernels and arithmetic), with one difference in
- * the variant: windows shorter than 8192 keys carry Q and P' as two e4m3
- * terms, and in this mode the choice follows the shortest possible window
- * (one chunk) instead of the current one.
+ * the host-state calls' (same kernels and arithmetic; with prob_terms 1 the
+ * two-term variant, which host-state calls take on windows under 8192 keys,
+ * follows the shortest possible window, one chunk, instead of the current
+ * one).
  * While the mode is on, rtv_cache_layout and rtv_cache_window report the
  * state as of rtv_device_state_begin, and the host checks only the argument
  * and call-order rules; a chunk past the end of the RoPE table makes the
