@@ -133,6 +133,10 @@ def pmc_summary(fetch_dir: str, write_dir: str, copy_bytes: int, out_json: str):
                     sums[key][disp] += float(row["Counter_Value"])
         per[counter] = {k: sum(v.values()) / len(v) for k, v in sums.items()}
         per[counter + "_dispatches"] = {k: len(v) for k, v in sums.items()}
+        if "copy" in sums:
+            # the calibration copy is the largest copy dispatch of the run (the
+            # runtime's small copies use the same kernel)
+            per[counter]["copy"] = max(sums["copy"].values())
     calib = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         kib = per[counter].get("copy")

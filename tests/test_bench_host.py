@@ -38,17 +38,20 @@ def _write_pmc(dirname, counter, rows):
 
 
 def test_pmc_summary_calibrates_by_the_copy_kernel():
-    """FETCH_SIZE of a 1 GiB copy reading half its bytes gives a factor of 2;
-    per-dispatch sums over counter instances are averaged over dispatches."""
+    """FETCH_SIZE of a 1 GiB copy reading half its bytes gives a factor of 2
+    (taken from the largest copy dispatch); per-dispatch sums over counter
+    instances are averaged over dispatches."""
     shutil.rmtree(BUILD, ignore_errors=True)
     att = "void rtv::(anonymous namespace)::attend16_kernel<false, false, false>(rtv::AttendArgs)"
     copy = "__amd_rocclr_copyBuffer"
     gib = 1 << 30
     fetch, write = os.path.join(BUILD, "fetch"), os.path.join(BUILD, "write")
     # two dispatches of the attention, each reported as two counter instances
+    # the runtime's own small copies use the copy kernel too: the calibration
+    # is the largest copy dispatch, not their mean
     _write_pmc(fetch, "FETCH_SIZE", [(1, att, 100.0), (1, att, 300.0), (2, att, 500.0), (2, att, 100.0),
-                                     (3, copy, gib / 1024 / 2)])
-    _write_pmc(write, "WRITE_SIZE", [(1, att, 10.0), (2, att, 30.0), (3, copy, gib / 1024)])
+                                     (3, copy, gib / 1024 / 2), (4, copy, 2.0)])
+    _write_pmc(write, "WRITE_SIZE", [(1, att, 10.0), (2, att, 30.0), (3, copy, gib / 1024), (4, copy, 0.0)])
     out = os.path.join(BUILD, "traffic.json")
     bench.pmc_summary(fetch, write, gib, out)
     with open(out) as f:
