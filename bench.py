@@ -52,8 +52,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the other workloads' figures (stress ring, GQA, projection) in the default line")
-    p.add_argument("--config-steps", type=int, default=3,
+    p.add_argument("--config-steps", type=int, default=10,
                    help="timed calls per figure of the other workloads in the default line")
+    p.add_argument("--config-warmup", type=int, default=5,
+                   help="untimed calls before each such figure (the clock ramps up after the host-side set-up)")
     p.add_argument("--eager", action="store_true",
                    help="time eagerly launched steps (default: replays of one captured HIP graph per step)")
     p.add_argument("--workload", choices=["step", "projection", "attention"], default="step",
@@ -682,7 +684,7 @@ def main():
         del cache
         torch.cuda.empty_cache()
         sub = argparse.Namespace(**vars(args))
-        sub.steps, sub.warmup = args.config_steps, 1
+        sub.steps, sub.warmup = args.config_steps, args.config_warmup
         att = attention_configs(sub)
         result["configs"] = {"stress_ring": att["stress"], "gqa_95744_keys": att["gqa"],
                              "layer_full_window_by_weights": att["layer_full_window"],

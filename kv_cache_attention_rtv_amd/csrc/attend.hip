@@ -25,7 +25,9 @@
 //   16 keys of 2 queries, which halves its per-key factor reads, and P' is
 //   brought to the PV operand layout by v_permlane16_swap (see there);
 //   O^T[d][query] += V^T . P'^T           D/32 d sub-tiles (32x32x64)
-//   L[r][query]   += U . P'^T             one product: the row sum
+//   L[r][query]   += U . P'^T             one product: the row sum (32x32x64
+//                                         for head dim 64; for head dim 128 a
+//                                         16x16x128 on the same P' registers)
 // Scores: each query carries its own power-of-two scale 2^e_q (its largest
 // rotated element maps into [128, 256)), applied exactly by the matrix core
 // through the E8M0 scale of the query operand, so the score products come out
@@ -121,6 +123,9 @@ __device__ __forceinline__ v4f mfma16_fp8(const v8i& a, const v8i& b, const v4f&
 }
 __device__ __forceinline__ v4f mfma16_fp8_bscaled(const v8i& a, const v8i& b, const v4f& c, int e) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, e);
+}
+__device__ __forceinline__ v4f mfma16_fp8_scaled(const v8i& a, const v8i& b, const v4f& c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
 
 // the same with the B operand scaled by 2^(e - 127) (E8M0 exponent e):
@@ -1147,13 +1152,19 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
       }
     }
   };
-  // O^T += V^T . P'^T and the row sum, as in attend_kernel
+  // O^T += V^T . P'^T as in attend_kernel.  The row sum is one 16x16x128
+  // product with the same B operand read in that product's layout: lane
+  // (q4, i) holds the codes of query 16 (q4 & 1) + i for the keys of half
+  // q4 >> 1, so column i sums queries i (k-blocks 0, 2) and 16 + i (k-blocks
+  // 1, 3).  A rows 0 / 2 carry U_hi / U_lo on k-blocks 0 and 2, rows 1 / 3 on
+  // k-blocks 1 and 3 (every other lane reads the zero row), and lane (0, i)
+  // accumulates (L_hi(i), L_hi(16 + i), L_lo(i), L_lo(16 + i)).
   v16f acc_o[NDT];
-  v16f acc_l = v16f{};
+  v4f acc_l = v4f{};
   v16f acc_g = v16f{};                      // P' P'^T (peaked-row check)
 #pragma unroll
   for (int d = 0; d < NDT; ++d) acc_o[d] = v16f{};
-  const int u_off = SM::U_OFF + (li < 2 ? li : 2) * SM::VROW + 32 * hh;
+  const int u_off = SM::U_OFF + ((i16 < 4 && (i16 & 1) == (q4 & 1)) ? (i16 >> 1) : 2) * SM::VROW + 32 * (q4 >> 1);
   auto load_v = [&](const uint8_t* st, v8i (&vop)[NDT + 1]) {
 #pragma unroll
     for (int d = 0; d <= NDT; ++d) {
@@ -1169,8 +1180,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
       acc_o[j] = mfma_fp8_scaled(vop[j], pop, acc_o[j], 127, ev);
       if constexpr (PLO) acc_o[j] = mfma_fp8_scaled(vop[j], plo, acc_o[j], 127, ev - kLoShift);
     } else {
-      acc_l = mfma_fp8_scaled(vop[NDT], pop, acc_l, 127 + 2, 127);
-      if constexpr (PLO) acc_l = mfma_fp8_scaled(vop[NDT], plo, acc_l, 127 + 2, 127 - kLoShift);
+      acc_l = mfma16_fp8_scaled(vop[NDT], pop, acc_l, 127 + 2, 127);
+      if constexpr (PLO) acc_l = mfma16_fp8_scaled(vop[NDT], plo, acc_l, 127 + 2, 127 - kLoShift);
       if constexpr (STAT) acc_g = mfma_fp8(pop, pop, acc_g);
     }
   };
@@ -1304,7 +1315,7 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
         const float al = (q4 & 1) ? alpha[1] : alpha[0];
 #pragma unroll
         for (int d = 0; d < NDT; ++d) acc_o[d] *= al;
-        acc_l *= al;
+        acc_l *= v4f{alpha[0], alpha[1], alpha[0], alpha[1]};
         if constexpr (STAT) acc_g *= al * al;
       }
     }
@@ -1342,7 +1353,8 @@ __global__ __launch_bounds__(kThreads, RTV_ATTEND_WG_PER_CU) void attend16_kerne
   }
 
   // ---- epilogue (PV layout: lane (hh, li) holds query li, the query block q4 & 1)
-  const float l_tot = xhalf_sum(acc_l[0] + acc_l[1]);
+  const float l_x = __shfl(acc_l[0] + acc_l[2], i16), l_y = __shfl(acc_l[1] + acc_l[3], i16);
+  const float l_tot = li < 16 ? l_x : l_y;
   const float g = STAT ? gram_diag(acc_g, li, hh) : 0.0f;
   write_result<D, LU>(a, acc_o, l_tot, (q4 & 1) ? m_run[1] : m_run[0], g, part, wave * kQPW + li, wrow + li, head,
                       hh);
