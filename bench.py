@@ -666,6 +666,32 @@ def main():
         "wall_s_timed": round(wall, 3),
         "recomputed_units_last_call": cache.peaked_units(stream=stream),
     }
+    # a plain streaming reference for the append's traffic: torch's elementwise
+    # add of each layer's K and V into one bf16 tensor reads the same 73.5 MB
+    # and writes 36.8 MB (the codes' bytes, without the scales and the RoPE
+    # table), one launch per layer on the same cold inputs, events around each
+    ref_out = torch.empty_like(inputs[0][1])
+    ref_ev = []
+    for _ in range(2):
+        for layer in range(wl.n_layers):
+            a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_ev.record(stream)
+            torch.add(inputs[layer][1], inputs[layer][2], out=ref_out)
+            b_ev.record(stream)
+            ref_ev.append((a_ev, b_ev))
+    torch.cuda.synchronize()
+    ref_ms = sorted(a_ev.elapsed_time(b_ev) for a_ev, b_ev in ref_ev[wl.n_layers:])
+    ref_bytes = 3 * inputs[0][1].numel() * 2
+    ref_avg = sum(ref_ms) / len(ref_ms)
+    result["append_roofline"]["streaming_reference"] = {
+        "kernel": "torch.add(K, V) into bf16 (one elementwise launch per layer, cold inputs)",
+        "bytes_per_launch": ref_bytes, "avg_launch_ms": round(ref_avg, 5),
+        "median_launch_ms": round(ref_ms[len(ref_ms) // 2], 5),
+        "achieved": round(ref_bytes / (ref_avg * 1e-3) / 1e9, 1),
+        "frac": round(ref_bytes / (ref_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "append_time_over_reference": round(app_avg_ms / ref_avg, 3),
+    }
+    del ref_out
     if args.copy_calibration:
         nb = args.copy_calibration << 20
         src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)

@@ -17,7 +17,10 @@
 // the global loads of stage t+1 are in flight while stage t is computed.
 // Tiles are numbered XCD-aware (each XCD walks a contiguous range) and grouped
 // four M-rows at a time so the workgroups resident on one XCD share operands
-// in its L2.
+// in its L2.  With one workgroup per compute unit the tiles run in whole
+// rounds; a last round that would fill at most half the device runs as
+// 256 x 128 half tiles in a second launch (twice the workgroups, half the
+// time).
 //
 // Fused QKV epilogue (gemm_fp8_kernel<D>, D = head_dim): the output columns
 // are [Q heads | K heads | V heads] of one chunk's tokens.  Q columns are
@@ -48,9 +51,11 @@ constexpr int kBM = 256, kBN = 256, kBK = 128;
 constexpr int kGemmWaves = 8;
 constexpr int kGemmThreads = kGemmWaves * kWave;
 constexpr int kRow = kBK + 16;                       // padded LDS row (bytes)
-constexpr int kStageBytes = (kBM + kBN) * kRow;      // 73728
 constexpr int kGroupM = 4;
-constexpr int kChunksPerThread = (kBM + kBN) * (kBK / 16) / kGemmThreads;  // 8
+// A launch of BN-wide tiles (BN = kBN, or kBN / 2 for the tiles of a last,
+// partial round): LDS bytes of one stage and 16-byte chunks per thread
+template <int BN> constexpr int stage_bytes() { return (kBM + BN) * kRow; }   // 73728 / 55296
+template <int BN> constexpr int chunks_per_thread() { return (kBM + BN) * (kBK / 16) / kGemmThreads; }
 
 constexpr int kQuantThreads = 256;
 
@@ -157,6 +162,8 @@ struct GemmArgs {
   int64_t ldc;
   int32_t M, N, K;
   int32_t n_mt, n_nt, n_tiles;
+  int32_t tile_base;   // first logical tile of the launch
+  int32_t n_launch;    // work items of the launch (tiles, or half tiles)
   int32_t vec_store;   // 8-byte stores allowed (c 8-aligned, ldc % 4 == 0)
   // fused QKV epilogue: columns [0, q_cols) are Q (bf16 into c), then
   // n_kv_heads K heads and n_kv_heads V heads of D columns into the ring
@@ -174,13 +181,15 @@ struct GemmArgs {
 // global -> register loads of one stage: chunk c of 16 bytes, rows [0, 256)
 // of A then of Bt, 8 chunks per row; rows past M / N repeat the last row and
 // k past K reads zeros
+template <int BN>
 struct StageRegs {
-  uint4 r[kChunksPerThread];
+  uint4 r[chunks_per_thread<BN>()];
 };
 
-__device__ __forceinline__ void load_stage(StageRegs& s, const GemmArgs& g, int m0, int n0, int k0) {
+template <int BN>
+__device__ __forceinline__ void load_stage(StageRegs<BN>& s, const GemmArgs& g, int m0, int n0, int k0) {
 #pragma unroll
-  for (int j = 0; j < kChunksPerThread; ++j) {
+  for (int j = 0; j < chunks_per_thread<BN>(); ++j) {
     const int c = threadIdx.x + j * kGemmThreads;
     const int row = c >> 3;                 // 0..511
     const int col = (c & 7) * 16;
@@ -194,9 +203,10 @@ __device__ __forceinline__ void load_stage(StageRegs& s, const GemmArgs& g, int 
   }
 }
 
-__device__ __forceinline__ void store_stage(const StageRegs& s, uint8_t* st) {
+template <int BN>
+__device__ __forceinline__ void store_stage(const StageRegs<BN>& s, uint8_t* st) {
 #pragma unroll
-  for (int j = 0; j < kChunksPerThread; ++j) {
+  for (int j = 0; j < chunks_per_thread<BN>(); ++j) {
     const int c = threadIdx.x + j * kGemmThreads;
     *reinterpret_cast<uint4*>(st + (c >> 3) * kRow + (c & 7) * 16) = s.r[j];
   }
@@ -214,19 +224,21 @@ __device__ __forceinline__ v8i frag(const uint8_t* st, int row0, int ks, int lan
   return v;
 }
 
-constexpr int kEpiRow = kBN * 4 + 16;          // bytes per token row of the f32 tile in LDS
-constexpr int kEpiAmax = 128 * kEpiRow;         // per-row amax exchange after the tile
+// bytes per token row of the f32 tile in LDS, and the per-row amax exchange after it
+template <int BN> constexpr int epi_row() { return BN * 4 + 16; }
+template <int BN> constexpr int epi_amax() { return 128 * epi_row<BN>(); }
 
-// Fused epilogue of one 256 x 256 tile (see the file comment).  acc[i][j]
+// Fused epilogue of one 256 x BN tile (see the file comment).  acc[i][j]
 // holds D[n][m] for m = m0+wm+32i + lane%32 and n = n0+wn+32j + 8(r/4) +
 // 4(lane/32) + r%4; tokens m >= M are skipped.
-template <int D, typename Acc>
+template <int D, int BN, typename Acc>
 __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc, float s, uint8_t* smem,
                                                int m0, int n0, int wm, int wn, int wave, int lane) {
   constexpr int HALF = D / 2;
   constexpr int PARTS = D / 64;                  // waves per head (32 RoPE pairs each)
+  constexpr int kEpiRow = epi_row<BN>();
   const int hh = lane >> 5;
-  float* amax_x = reinterpret_cast<float*>(smem + kEpiAmax);
+  float* amax_x = reinterpret_cast<float*>(smem + epi_amax<BN>());
   const int kv_cols = g.n_kv_heads * D;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -236,7 +248,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
     for (int ii = 0; ii < 2; ++ii) {
       const int row = (wm / 128) * 64 + ii * 32 + (lane & 31);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < BN / 128; ++j)
 #pragma unroll
         for (int grp4 = 0; grp4 < 4; ++grp4) {
           const int n = wn + 32 * j + 8 * grp4 + 4 * hh;
@@ -246,7 +258,9 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
         }
     }
     __syncthreads();
-    // (2) wave -> (ring tile t, head of the tile, part); lane -> token
+    // (2) wave -> (ring tile t, head of the tile, part); lane -> token (a
+    // BN = 128 tile holds half the heads: the other waves only take part in
+    // the barriers)
     const int t = wave >> 2;
     const int hp = wave & 3;
     const int head_local = hp / PARTS;
@@ -254,7 +268,9 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
     const int m = m0 + 128 * t + 64 * half + lane;
     const bool valid = m < g.M;
     const int col = n0 + head_local * D;         // first column of the head (uniform)
-    const float* erow = reinterpret_cast<const float*>(smem + (64 * t + lane) * kEpiRow) + head_local * D;
+    const bool in_tile = head_local * D < BN;
+    const float* erow =
+        reinterpret_cast<const float*>(smem + (64 * t + lane) * kEpiRow) + (in_tile ? head_local : 0) * D;
     float x0[32], x1[32];
 #pragma unroll
     for (int q = 0; q < 32; q += 4) {
@@ -265,7 +281,7 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
     }
     const bool is_q = col < g.q_cols;
     const bool is_k = !is_q && col < g.q_cols + kv_cols;
-    const bool in_range = col < g.N;
+    const bool in_range = col < g.N && in_tile;
     if (is_k) {
       // RoPE at position (chunk start) + m, rounded as in the append
       const float* cs = g.rope + (int64_t)(valid ? m : 0) * D + 64 * part;
@@ -338,11 +354,18 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
   }
 }
 
-template <int FUSED_D>
+// BN = kBN: work item = logical tile tile_base + item.  BN = kBN / 2: the
+// tiles of a last, partial round as two halves each (item = 2 x tile +
+// half), so that twice as many workgroups share that round's work.
+template <int FUSED_D, int BN>
 __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
+  static_assert(BN == kBN || 2 * BN == kBN, "full or half tiles");
+  constexpr int NJ = BN / 128;              // 32-column blocks per wave
+  constexpr int kStageBytes = stage_bytes<BN>();
   extern __shared__ __align__(16) uint8_t smem[];
-  const int logical = xcd_remap(blockIdx.x, g.n_tiles);
-  if (logical < 0) return;
+  const int item = xcd_remap(blockIdx.x, g.n_launch);
+  if (item < 0) return;
+  const int logical = g.tile_base + (BN == kBN ? item : item >> 1);
   // group kGroupM tile rows: consecutive logical tiles walk down a column of
   // the group first
   const int group_size = kGroupM * g.n_nt;
@@ -352,43 +375,43 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
   const int in_grp = logical - grp * group_size;
   const int mt = first_m + in_grp % gm;
   const int nt = in_grp / gm;
-  const int m0 = mt * kBM, n0 = nt * kBN;
+  const int m0 = mt * kBM, n0 = nt * kBN + (BN == kBN ? 0 : (item & 1) * BN);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int wm = (wave & 1) * 128;      // wave's M offset in the tile
-  const int wn = (wave >> 1) * 64;      // wave's N offset in the tile
+  const int wn = (wave >> 1) * (BN / 4);  // wave's N offset in the tile
 
-  v16f acc[4][2];
+  v16f acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int n_k = (g.K + kBK - 1) / kBK;
-  StageRegs regs;
-  load_stage(regs, g, m0, n0, 0);
+  StageRegs<BN> regs;
+  load_stage<BN>(regs, g, m0, n0, 0);
   store_stage(regs, smem);
   __syncthreads();
   for (int t = 0; t < n_k; ++t) {
     const bool more = t + 1 < n_k;
-    if (more) load_stage(regs, g, m0, n0, (t + 1) * kBK);
+    if (more) load_stage<BN>(regs, g, m0, n0, (t + 1) * kBK);
     const uint8_t* st = smem + (t & 1) * kStageBytes;
     const uint8_t* sa = st;                 // A rows
     const uint8_t* sbt = st + kBM * kRow;   // Bt rows
 #pragma unroll
     for (int ks = 0; ks < kBK / 64; ++ks) {
-      v8i bop[2], aop[4];
+      v8i bop[NJ], aop[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bop[j] = frag(sbt, wn + 32 * j, ks, lane);
+      for (int j = 0; j < NJ; ++j) bop[j] = frag(sbt, wn + 32 * j, ks, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) aop[i] = frag(sa, wm + 32 * i, ks, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_fp8(bop[j], aop[i], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_fp8(bop[j], aop[i], acc[i][j]);
     }
     if (more) store_stage(regs, smem + ((t + 1) & 1) * kStageBytes);
     __syncthreads();
@@ -398,7 +421,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
   // n = n0+wn+32j + 8(r/4) + 4(lane/32) + r%4
   const float s = (*g.sa) * (*g.sb);
   if constexpr (FUSED_D > 0) {
-    fused_epilogue<FUSED_D>(g, acc, s, smem, m0, n0, wm, wn, wave, lane);
+    fused_epilogue<FUSED_D, BN>(g, acc, s, smem, m0, n0, wm, wn, wave, lane);
     return;
   }
   const int hh = lane >> 5;
@@ -408,7 +431,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
     if (m >= g.M) continue;
     uint16_t* crow = g.c + (int64_t)m * g.ldc;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
 #pragma unroll
       for (int grp4 = 0; grp4 < 4; ++grp4) {
         const int n = n0 + wn + 32 * j + 8 * grp4 + 4 * hh;
@@ -498,14 +521,71 @@ static GemmArgs gemm_args(const uint8_t* a, const float* sa, const uint8_t* bt, 
   return g;
 }
 
-template <int FUSED_D>
-static hipError_t launch_gemm(const GemmArgs& g, hipStream_t stream) {
-  const hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<FUSED_D>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kStageBytes);
+// LDS of a launch: the two operand stages, or the fused epilogue's f32 tile
+// and amax exchange if larger
+template <int FUSED_D, int BN>
+constexpr int gemm_lds_bytes() {
+  return FUSED_D > 0 && epi_amax<BN>() + kGemmWaves * 64 * 4 > 2 * stage_bytes<BN>()
+             ? epi_amax<BN>() + kGemmWaves * 64 * 4
+             : 2 * stage_bytes<BN>();
+}
+
+template <int FUSED_D, int BN>
+static hipError_t launch_part(const GemmArgs& g, hipStream_t stream) {
+  constexpr int lds = gemm_lds_bytes<FUSED_D, BN>();
+  static_assert(lds <= 160 * 1024, "one workgroup's LDS");
+  const hipError_t e = hipFuncSetAttribute((const void*)gemm_fp8_kernel<FUSED_D, BN>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  const int grid = (g.n_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL(gemm_fp8_kernel<FUSED_D>, dim3(grid), dim3(kGemmThreads), 2 * kStageBytes, stream, g);
+  const int grid = (g.n_launch + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_fp8_kernel<FUSED_D, BN>), dim3(grid), dim3(kGemmThreads), lds, stream, g);
   return hipGetLastError();
+}
+
+// compute units of the current device (one GEMM workgroup each), looked up
+// once per device
+static hipError_t device_cus(int* out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int cus[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    e = hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  *out = cus[dev];
+  return hipSuccess;
+}
+
+// Whole rounds of 256 x 256 tiles (one workgroup per compute unit), then the
+// tiles of a last round that would fill at most half the device as 256 x 128
+// halves: that round then takes about half a tile's time instead of a whole
+// one (846 tiles on 256 units: 3 rounds + 78 tiles, the projection chunk).
+template <int FUSED_D>
+static hipError_t launch_gemm(GemmArgs g, hipStream_t stream) {
+  int cus = 0;
+  hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  const int full = cus > 0 ? g.n_tiles / cus * cus : g.n_tiles;
+  const int rem = g.n_tiles - full;
+  if (rem == 0 || 2 * rem > cus) {
+    g.tile_base = 0;
+    g.n_launch = g.n_tiles;
+    return launch_part<FUSED_D, kBN>(g, stream);
+  }
+  if (full > 0) {
+    g.tile_base = 0;
+    g.n_launch = full;
+    e = launch_part<FUSED_D, kBN>(g, stream);
+    if (e != hipSuccess) return e;
+  }
+  g.tile_base = full;
+  g.n_launch = 2 * rem;
+  return launch_part<FUSED_D, kBN / 2>(g, stream);
 }
 
 hipError_t launch_gemm_fp8(const uint8_t* a, const float* sa, const uint8_t* bt, const float* sb,
@@ -514,7 +594,6 @@ hipError_t launch_gemm_fp8(const uint8_t* a, const float* sa, const uint8_t* bt,
 }
 
 hipError_t launch_qkv_gemm_append(const QkvAppendArgs& q, hipStream_t stream) {
-  static_assert(2 * kStageBytes >= kEpiAmax + kGemmWaves * 64 * 4, "fused epilogue fits the GEMM's LDS");
   const int N = q.q_cols + 2 * q.n_kv_heads * q.head_dim;
   GemmArgs g = gemm_args(q.x, q.sx, q.wt, q.sw, q.q_out, q.M, N, q.K, q.ldq);
   g.q_cols = q.q_cols;
