@@ -151,6 +151,27 @@ def test_gemm_ragged_shapes(rtv_lib, M, N, K):
     _check_gemm(_np_bits(out), a, sa, bt.T, sb, min_same=0.9)
 
 
+@pytest.mark.parametrize("M,N,K", [(8192, 4096, 128),     # 512 tiles of 256 x 256: two whole rounds
+                                   (6400, 4608, 192),     # 450 tiles: the last round over half full, one launch
+                                   (4200, 4608, 128)])    # 306 tiles: the last 50 as 100 half tiles
+def test_gemm_round_structure(rtv_lib, M, N, K):
+    """Sampled rows (the first and last of every 256-row band) of GEMMs whose
+    tile count ends in a whole round, in a last round run as it is, and in a
+    last round run as half tiles (on a 256-unit device)."""
+    rng = np.random.default_rng(M + N + K)
+    a = _random_codes(rng, (M, K))
+    bt = _random_codes(rng, (N, K))
+    sa, sb = np.float32(0.0123), np.float32(3.7e-3)
+    print(f"gemm rounds M={M} N={N} K={K}", flush=True)
+    dev = torch.device("cuda")
+    out = rtv_lib.gemm_fp8(torch.from_numpy(a).to(dev), torch.tensor([sa], dtype=torch.float32, device=dev),
+                           torch.from_numpy(bt).to(dev), torch.tensor([sb], dtype=torch.float32, device=dev))
+    bands = np.arange(0, M, 256)
+    rows = np.unique(np.concatenate([bands, np.minimum(bands + 255, M - 1), rng.integers(0, M, 16)]))
+    got = _np_bits(out[torch.as_tensor(rows, device=dev)])
+    _check_gemm(got, a[rows], sa, bt.T, sb, min_same=0.9)
+
+
 def test_gemm_strided_output_and_errors(rtv_lib):
     rng = np.random.default_rng(5)
     M, N, K, ldc = 130, 70, 128, 77         # odd row stride: element stores
