@@ -88,7 +88,7 @@ typedef struct rtv_config {
                               * tolerance on peaked rows (a few keys carrying much of the
                               * weight);
                               * 2: two terms on every window, for callers that know their
-                              * attention is peaked (about 1.9 times the one-code time on
+                              * attention is peaked (about 1.8 times the one-code time on
                               * a 47872-key window). */
   double rope_base;          /* RoPE base (10000) */
   const float* rope_cos_sin_host;
