@@ -15,9 +15,10 @@
 // [g*E, g*E+E) and [D/2+g*E, D/2+g*E+E), E = D/16, i.e. both halves of its
 // RoPE pairs, so the rotation needs no lane exchange and every bf16 load is
 // 8 lanes x 16 B = 128 B contiguous.  The row amax is an 8-lane DPP max.
-// K codes go straight to their row; V codes go through LDS and are written
-// transposed per tile ([d][64 slots], key order of the attention kernel's
-// matrix-core operand), 64 contiguous bytes per d-row.
+// K codes go straight to their row, 16 bytes per lane; V codes go through
+// LDS and are written transposed per tile ([d][64 slots], key order of the
+// attention kernel's matrix-core operand), 16 bytes per lane.  The bf16
+// inputs are read with non-temporal loads.
 //
 // Arithmetic is fixed bit for bit: RoPE products and the sum/difference are
 // rounded separately (no contraction: this file is built with
@@ -62,23 +63,29 @@ struct RowPiece {
   uint32_t w0[E / 2], w1[E / 2];
 };
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// K and V are read once per call: the loads are non-temporal, so that the
+// chunk's 74 MB of bf16 input streams past the caches instead of evicting the
+// RoPE rows, which the append of every layer reads again.
 template <int D>
 __device__ __forceinline__ RowPiece<D / 16> load_piece(const uint16_t* row, int g, bool valid) {
   constexpr int E = D / 16;
   RowPiece<E> r;
   if constexpr (E == 8) {
-    uint4 p0 = make_uint4(0, 0, 0, 0), p1 = p0;
+    u32x4_t p0 = {0, 0, 0, 0}, p1 = p0;
     if (valid) {
-      p0 = *(const uint4*)(row + g * E);
-      p1 = *(const uint4*)(row + D / 2 + g * E);
+      p0 = __builtin_nontemporal_load((const u32x4_t*)(row + g * E));
+      p1 = __builtin_nontemporal_load((const u32x4_t*)(row + D / 2 + g * E));
     }
     r.w0[0] = p0.x; r.w0[1] = p0.y; r.w0[2] = p0.z; r.w0[3] = p0.w;
     r.w1[0] = p1.x; r.w1[1] = p1.y; r.w1[2] = p1.z; r.w1[3] = p1.w;
   } else {
-    uint2 p0 = make_uint2(0, 0), p1 = p0;
+    u32x2_t p0 = {0, 0}, p1 = p0;
     if (valid) {
-      p0 = *(const uint2*)(row + g * E);
-      p1 = *(const uint2*)(row + D / 2 + g * E);
+      p0 = __builtin_nontemporal_load((const u32x2_t*)(row + g * E));
+      p1 = __builtin_nontemporal_load((const u32x2_t*)(row + D / 2 + g * E));
     }
     r.w0[0] = p0.x; r.w0[1] = p0.y;
     r.w1[0] = p1.x; r.w1[1] = p1.y;
@@ -138,7 +145,8 @@ __global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(
   // ---- global loads ahead of the arithmetic: the K and V pieces of the first
   // two heads and, once for all heads, the row's RoPE (cos, sin); the pieces
   // of head j + 2 are loaded once head j is done, so at most two heads' pieces
-  // are live (79 VGPRs: three workgroups per CU, the whole chunk in one round)
+  // are live (80 VGPRs, three workgroups per CU, the whole chunk in one round;
+  // only the general quantization path of rows with a subnormal scale spills)
   RowPiece<E> kp[HPW], vp[HPW];
   auto load_head = [&](int j) {
     const bool hv = h0 + j < a.n_heads;
@@ -186,11 +194,20 @@ __global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(
       amax = dpp_max8(amax);
       uint32_t c0[E / 4], c1[E / 4];
       const float ks = quant_row<E>(r0, r1, c0, c1, amax, __all(!valid || fast_amax(amax)));
+      // (D = 128: adjacent lanes swap halves, so that each lane stores 16
+      // contiguous bytes: the even lane both first-half pieces, the odd lane
+      // both second-half pieces)
+      uint32_t x0 = 0, x1 = 0;
+      const bool odd = g & 1;
+      if constexpr (E == 8) {
+        x0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? c0[0] : c1[0]), 0xB1, 0xF, 0xF, false);
+        x1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? c0[1] : c1[1]), 0xB1, 0xF, 0xF, false);
+      }
       if (valid) {
         uint8_t* dst = a.kc + ((int64_t)h * a.slots_padded + slot) * D;
         if constexpr (E == 8) {
-          *(uint2*)(dst + g * E) = make_uint2(c0[0], c0[1]);
-          *(uint2*)(dst + HALF + g * E) = make_uint2(c1[0], c1[1]);
+          uint8_t* p = dst + (odd ? HALF + (g - 1) * E : g * E);
+          *(uint4*)p = odd ? make_uint4(x0, x1, c1[0], c1[1]) : make_uint4(c0[0], c0[1], x0, x1);
         } else {
           *(uint32_t*)(dst + g * E) = c0[0];
           *(uint32_t*)(dst + HALF + g * E) = c1[0];
@@ -224,45 +241,53 @@ __global__ __launch_bounds__(kAppendThreads) __attribute__((amdgpu_waves_per_eu(
   __syncthreads();
 
   // ---- V: transposed write of each head's tile ----------------------------
-  // Thread block (p4, dq): positions 4*p4..4*p4+3 (4 consecutive keys) x
-  // d = 4*dq..4*dq+3; a 4x4 byte transpose turns 4 key rows into 4 d rows.
+  // Thread (q, dq) of a head: positions 16q..16q+15 (four runs of 4
+  // consecutive keys) x d = 4dq..4dq+3; four 4x4 byte transposes turn the
+  // 16 key rows into 4 d rows of 16 bytes, one 16-byte store each.
   const bool full = (lo == tile_lo) && (hi == tile_lo + kTileKeys);
-  constexpr int kBlocks = 16 * (D / 4);
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
+  constexpr int kBlocks = 4 * (D / 4);   // per head
+  const int n_here = (a.n_heads - h0) < HPW ? (a.n_heads - h0) : HPW;
+  for (int id = tid; id < n_here * kBlocks; id += kAppendThreads) {
+    const int j = id / kBlocks;
     const int h = h0 + j;
-    if (h >= a.n_heads) break;
+    const int w = id - j * kBlocks;
+    const int q = w & 3;
+    const int dq = w >> 2;
     uint8_t* vt = a.vc + (((int64_t)h * (a.slots_padded / kTileKeys) + st) * D) * kTileKeys;
+    uint32_t o[4][4];
 #pragma unroll
-    for (int id = tid; id < kBlocks; id += kAppendThreads) {
-      const int p4 = id & 15;
-      const int dq = id >> 4;
-      const int key0 = vt_key_of_pos4(p4);
-      const uint32_t a0 = vrow[j][(key0 + 0) * (LDS_STRIDE / 4) + dq];
-      const uint32_t a1 = vrow[j][(key0 + 1) * (LDS_STRIDE / 4) + dq];
-      const uint32_t a2 = vrow[j][(key0 + 2) * (LDS_STRIDE / 4) + dq];
-      const uint32_t a3 = vrow[j][(key0 + 3) * (LDS_STRIDE / 4) + dq];
+    for (int sub = 0; sub < 4; ++sub) {
+      const int key0 = vt_key_of_pos4(4 * q + sub);
+      const uint32_t* base = vrow[j] + key0 * (LDS_STRIDE / 4) + dq;
+      const uint32_t a0 = base[0];
+      const uint32_t a1 = base[LDS_STRIDE / 4];
+      const uint32_t a2 = base[2 * (LDS_STRIDE / 4)];
+      const uint32_t a3 = base[3 * (LDS_STRIDE / 4)];
       const uint32_t lo01 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);
       const uint32_t hi01 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);
       const uint32_t lo23 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
       const uint32_t hi23 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-      const uint32_t o[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
-                             __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
-                             __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
-                             __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
-      if (full) {
+      o[0][sub] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+      o[1][sub] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+      o[2][sub] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+      o[3][sub] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+    }
+    if (full) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *(uint32_t*)(vt + (int64_t)(4 * dq + e) * kTileKeys + 4 * p4) = o[e];
-      } else {
-        // partial tile (chunk not aligned to 64 slots): write only this chunk's keys
+      for (int e = 0; e < 4; ++e)
+        *(uint4*)(vt + (int64_t)(4 * dq + e) * kTileKeys + 16 * q) = make_uint4(o[e][0], o[e][1], o[e][2], o[e][3]);
+    } else {
+      // partial tile (chunk not aligned to 64 slots): write only this chunk's keys
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const int key0 = vt_key_of_pos4(4 * q + sub);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int64_t sl = tile_lo + key0 + c;
             if (sl >= lo && sl < hi)
-              vt[(int64_t)(4 * dq + e) * kTileKeys + 4 * p4 + c] = (uint8_t)(o[e] >> (8 * c));
+              vt[(int64_t)(4 * dq + e) * kTileKeys + 16 * q + 4 * sub + c] = (uint8_t)(o[e][sub] >> (8 * c));
           }
       }
     }
