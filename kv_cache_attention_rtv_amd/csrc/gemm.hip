@@ -8,9 +8,10 @@
 //   whole tensor as the row),
 //   C = bf16( (s_a * s_b) * sum_k dec(A[m,k]) * dec(B[k,n]) ), f32 accumulation.
 //
-// GEMM decomposition: one workgroup = a 256 x 256 tile of C, 8 waves in a
-// 2 (M) x 4 (N) grid, each wave 128 x 64 = 4 x 2 blocks of
-// v_mfma_f32_32x32x64_f8f6f4.  The Bt block is the MFMA A operand and the A
+// GEMM decomposition: one workgroup = a 256 x 256 tile of C, 16 waves in a
+// 4 (M) x 4 (N) grid, each wave 64 x 64 = 2 x 2 blocks of
+// v_mfma_f32_32x32x64_f8f6f4 (four waves per SIMD, so that one wave's
+// operand reads and barrier waits overlap the others' products).  The Bt block is the MFMA A operand and the A
 // block the B operand, so a lane of the result holds four consecutive output
 // columns of one row (one 8-byte bf16 store).  K advances 128 bytes per stage
 // through two LDS stages (rows padded to 144 B, conflict-free 16-byte reads);
@@ -31,10 +32,10 @@
 // fused FP8 matmul of page "Runway explains how it serves a 57B video model in
 // real time", fourth paragraph, with the write-time RoPE and FP8 of the same
 // paragraph).  The accumulator tile goes through LDS (f32, 128 tokens at a
-// time); then each wave takes one 64-token ring tile of one head, one lane per
-// token, so a row's RoPE pairs and amax stay in one lane (plus one exchange
-// between the two waves of a 128-wide head), K rows are written as 32-byte
-// runs and the transposed V tile as 64-byte rows.
+// time); then each wave takes 16 RoPE pairs of one head in one 64-token ring
+// tile, one lane per token, so a row's RoPE pairs stay in one lane and its
+// amax takes one exchange through LDS between the waves of the head; K rows
+// are written as 16-byte runs and the transposed V tile as 64-byte rows.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -48,7 +49,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 128;
-constexpr int kGemmWaves = 8;
+constexpr int kGemmWaves = 16;
 constexpr int kGemmThreads = kGemmWaves * kWave;
 constexpr int kRow = kBK + 16;                       // padded LDS row (bytes)
 constexpr int kGroupM = 4;
@@ -229,13 +230,14 @@ template <int BN> constexpr int epi_row() { return BN * 4 + 16; }
 template <int BN> constexpr int epi_amax() { return 128 * epi_row<BN>(); }
 
 // Fused epilogue of one 256 x BN tile (see the file comment).  acc[i][j]
-// holds D[n][m] for m = m0+wm+32i + lane%32 and n = n0+wn+32j + 8(r/4) +
-// 4(lane/32) + r%4; tokens m >= M are skipped.
+// (i < 2) holds D[n][m] for m = m0+wm+32i + lane%32 and n = n0+wn+32j +
+// 8(r/4) + 4(lane/32) + r%4; tokens m >= M are skipped.
 template <int D, int BN, typename Acc>
 __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc, float s, uint8_t* smem,
                                                int m0, int n0, int wm, int wn, int wave, int lane) {
   constexpr int HALF = D / 2;
-  constexpr int PARTS = D / 64;                  // waves per head (32 RoPE pairs each)
+  constexpr int PAIRS = 16;                      // RoPE pairs per lane
+  constexpr int PARTS = HALF / PAIRS;            // waves per head
   constexpr int kEpiRow = epi_row<BN>();
   const int hh = lane >> 5;
   float* amax_x = reinterpret_cast<float*>(smem + epi_amax<BN>());
@@ -243,26 +245,31 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();                             // LDS free: operands or the previous half consumed
-    // (1) the wave's tokens m0 + wm + 64 half + [0, 64) -> rows (wm / 128) * 64 + [0, 64)
+    // (1) tokens 64 half + [0, 64) and 128 + 64 half + [0, 64) of the tile ->
+    // rows [0, 64) and [64, 128): the waves whose 64 rows they are (wm = 64
+    // half or 128 + 64 half) write their accumulators
+    const int wblk = wm / 64;
+    if ((wblk & 1) == half) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int row = (wm / 128) * 64 + ii * 32 + (lane & 31);
+      for (int ii = 0; ii < 2; ++ii) {
+        const int row = (wblk >> 1) * 64 + ii * 32 + (lane & 31);
 #pragma unroll
-      for (int j = 0; j < BN / 128; ++j)
+        for (int j = 0; j < BN / 128; ++j)
 #pragma unroll
-        for (int grp4 = 0; grp4 < 4; ++grp4) {
-          const int n = wn + 32 * j + 8 * grp4 + 4 * hh;
-          const auto& a4 = acc[2 * half + ii][j];
-          *reinterpret_cast<float4*>(smem + row * kEpiRow + n * 4) =
-              make_float4(a4[4 * grp4] * s, a4[4 * grp4 + 1] * s, a4[4 * grp4 + 2] * s, a4[4 * grp4 + 3] * s);
-        }
+          for (int grp4 = 0; grp4 < 4; ++grp4) {
+            const int n = wn + 32 * j + 8 * grp4 + 4 * hh;
+            const auto& a4 = acc[ii][j];
+            *reinterpret_cast<float4*>(smem + row * kEpiRow + n * 4) =
+                make_float4(a4[4 * grp4] * s, a4[4 * grp4 + 1] * s, a4[4 * grp4 + 2] * s, a4[4 * grp4 + 3] * s);
+          }
+      }
     }
     __syncthreads();
-    // (2) wave -> (ring tile t, head of the tile, part); lane -> token (a
-    // BN = 128 tile holds half the heads: the other waves only take part in
-    // the barriers)
-    const int t = wave >> 2;
-    const int hp = wave & 3;
+    // (2) wave -> (ring tile t, head of the tile, part of PAIRS RoPE pairs);
+    // lane -> token.  (In a BN = 128 tile the waves of the heads outside it
+    // only take part in the barriers.)
+    const int t = wave / (kGemmWaves / 2);
+    const int hp = wave % (kGemmWaves / 2);
     const int head_local = hp / PARTS;
     const int part = hp % PARTS;
     const int m = m0 + 128 * t + 64 * half + lane;
@@ -271,11 +278,11 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
     const bool in_tile = head_local * D < BN;
     const float* erow =
         reinterpret_cast<const float*>(smem + (64 * t + lane) * kEpiRow) + (in_tile ? head_local : 0) * D;
-    float x0[32], x1[32];
+    float x0[PAIRS], x1[PAIRS];
 #pragma unroll
-    for (int q = 0; q < 32; q += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(erow + 32 * part + q);
-      const float4 b = *reinterpret_cast<const float4*>(erow + HALF + 32 * part + q);
+    for (int q = 0; q < PAIRS; q += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(erow + PAIRS * part + q);
+      const float4 b = *reinterpret_cast<const float4*>(erow + HALF + PAIRS * part + q);
       x0[q] = a.x; x0[q + 1] = a.y; x0[q + 2] = a.z; x0[q + 3] = a.w;
       x1[q] = b.x; x1[q + 1] = b.y; x1[q + 2] = b.z; x1[q + 3] = b.w;
     }
@@ -284,9 +291,9 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
     const bool in_range = col < g.N && in_tile;
     if (is_k) {
       // RoPE at position (chunk start) + m, rounded as in the append
-      const float* cs = g.rope + (int64_t)(valid ? m : 0) * D + 64 * part;
+      const float* cs = g.rope + (int64_t)(valid ? m : 0) * D + 2 * PAIRS * part;
 #pragma unroll
-      for (int q = 0; q < 32; q += 2) {
+      for (int q = 0; q < PAIRS; q += 2) {
         const float4 c = *reinterpret_cast<const float4*>(cs + 2 * q);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -303,20 +310,20 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
     }
     float amax = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fmaxf(fabsf(x0[q]), fabsf(x1[q])));
-    if constexpr (PARTS > 1) {
-      amax_x[wave * 64 + lane] = amax;
-      __syncthreads();
-      amax = fmaxf(amax, amax_x[(wave ^ 1) * 64 + lane]);
-    }
+    for (int q = 0; q < PAIRS; ++q) amax = fmaxf(amax, fmaxf(fabsf(x0[q]), fabsf(x1[q])));
+    // the row's amax over the PARTS waves of its head
+    amax_x[wave * 64 + lane] = amax;
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < PARTS; ++p) amax = fmaxf(amax, amax_x[(wave - part + p) * 64 + lane]);
     // rows with a normal scale take the short form of the quantization (one
     // uniform choice per wave, taken before the lanes of other rows leave)
     const bool fast = __all(!valid || !in_range || fast_amax(amax));
     if (!valid || !in_range) continue;
     if (is_q) {
-      uint16_t* dst = g.c + (int64_t)m * g.ldc + col + 32 * part;
+      uint16_t* dst = g.c + (int64_t)m * g.ldc + col + PAIRS * part;
 #pragma unroll
-      for (int q = 0; q < 32; q += 8) {
+      for (int q = 0; q < PAIRS; q += 8) {
         uint4 w0, w1;
         w0.x = pack_bf16x2(x0[q], x0[q + 1]); w0.y = pack_bf16x2(x0[q + 2], x0[q + 3]);
         w0.z = pack_bf16x2(x0[q + 4], x0[q + 5]); w0.w = pack_bf16x2(x0[q + 6], x0[q + 7]);
@@ -327,16 +334,14 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
       }
       continue;
     }
-    uint32_t c0[8], c1[8];
-    const float row_s = quant_row<32>(x0, x1, c0, c1, amax, fast);
+    uint32_t c0[PAIRS / 4], c1[PAIRS / 4];
+    const float row_s = quant_row<PAIRS>(x0, x1, c0, c1, amax, fast);
     const int64_t slot = g.write_slot + m;
     if (is_k) {
       const int h = (col - g.q_cols) / D;
-      uint8_t* dst = g.kc + ((int64_t)h * g.slots_padded + slot) * D + 32 * part;
+      uint8_t* dst = g.kc + ((int64_t)h * g.slots_padded + slot) * D + PAIRS * part;
       *reinterpret_cast<uint4*>(dst) = make_uint4(c0[0], c0[1], c0[2], c0[3]);
-      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(c0[4], c0[5], c0[6], c0[7]);
       *reinterpret_cast<uint4*>(dst + HALF) = make_uint4(c1[0], c1[1], c1[2], c1[3]);
-      *reinterpret_cast<uint4*>(dst + HALF + 16) = make_uint4(c1[4], c1[5], c1[6], c1[7]);
       if (part == 0) g.ks[(int64_t)h * g.slots_padded + slot] = row_s;
     } else {
       // transposed V tile: byte vt_pos(slot % 64) of row d; the wave's 64
@@ -345,9 +350,9 @@ __device__ __forceinline__ void fused_epilogue(const GemmArgs& g, const Acc& acc
       uint8_t* vt = g.vc + (((int64_t)h * (g.slots_padded / kTileKeys) + slot / kTileKeys) * D) * kTileKeys +
                     vt_pos_of_key((int)(slot % kTileKeys));
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
-        vt[(int64_t)(32 * part + q) * kTileKeys] = (uint8_t)(c0[q >> 2] >> (8 * (q & 3)));
-        vt[(int64_t)(HALF + 32 * part + q) * kTileKeys] = (uint8_t)(c1[q >> 2] >> (8 * (q & 3)));
+      for (int q = 0; q < PAIRS; ++q) {
+        vt[(int64_t)(PAIRS * part + q) * kTileKeys] = (uint8_t)(c0[q >> 2] >> (8 * (q & 3)));
+        vt[(int64_t)(HALF + PAIRS * part + q) * kTileKeys] = (uint8_t)(c1[q >> 2] >> (8 * (q & 3)));
       }
       if (part == 0) g.vs[(int64_t)h * g.slots_padded + slot] = row_s;
     }
@@ -379,12 +384,12 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int wm = (wave & 1) * 128;      // wave's M offset in the tile
-  const int wn = (wave >> 1) * (BN / 4);  // wave's N offset in the tile
+  const int wm = (wave & 3) * 64;       // wave's M offset in the tile
+  const int wn = (wave >> 2) * (BN / 4);  // wave's N offset in the tile
 
-  v16f acc[4][NJ];
+  v16f acc[2][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -403,13 +408,13 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
     const uint8_t* sbt = st + kBM * kRow;   // Bt rows
 #pragma unroll
     for (int ks = 0; ks < kBK / 64; ++ks) {
-      v8i bop[NJ], aop[4];
+      v8i bop[NJ], aop[2];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) bop[j] = frag(sbt, wn + 32 * j, ks, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) aop[i] = frag(sa, wm + 32 * i, ks, lane);
+      for (int i = 0; i < 2; ++i) aop[i] = frag(sa, wm + 32 * i, ks, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_fp8(bop[j], aop[i], acc[i][j]);
     }
@@ -426,7 +431,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
   }
   const int hh = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int m = m0 + wm + 32 * i + (lane & 31);
     if (m >= g.M) continue;
     uint16_t* crow = g.c + (int64_t)m * g.ldc;
