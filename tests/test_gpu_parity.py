@@ -77,12 +77,12 @@ def test_e4m3_conversion_matches_oracle(rtv_lib):
     assert bad.size == 0, [(float(y[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
 
 
-@pytest.mark.parametrize("group", [1, 2])
+@pytest.mark.parametrize("group", [1, 2, 3, 4])
 def test_tiny_stream_wraps(rtv_lib, group):
-    """12 chunks through an 8-frame ring (6 wraps), two calls per step, head_dim 64."""
+    """12 chunks through an 8-frame ring (6 wraps), two calls per step, head_dim
+    64; group query heads per KV head."""
     wl = get_workload("tiny")
-    if group == 2:
-        wl = dataclasses.replace(wl, n_q_heads=4)
+    wl = dataclasses.replace(wl, n_q_heads=wl.n_kv_heads * group)
     gpu, ora = _caches(rtv_lib, wl)
     worst = (0.0, 0.0)
     for step in range(wl.steps):
@@ -209,6 +209,7 @@ def test_state_errors(rtv_lib):
 @pytest.mark.parametrize("T,F,C,D,H,Hq,steps", [
     (100, 2, 6, 128, 2, 4, 7),      # 200-token chunks: ragged 64-slot tiles, short windows
     (100, 2, 6, 64, 2, 2, 7),
+    (100, 2, 6, 128, 1, 4, 5),      # four query heads per KV head
     (2000, 2, 6, 128, 1, 2, 5),     # 4000-token chunks: ragged tiles, windows >= 8192 keys
 ])
 def test_unaligned_chunks(rtv_lib, T, F, C, D, H, Hq, steps):
