@@ -250,8 +250,9 @@ def projection(args):
     """The projection workload's chunk: X [11968 x 6144] bf16 to e4m3 (per
     tensor), then either the FP8 GEMM to bf16 QKV [11968 x 4608] followed by
     the append of its K/V columns (unfused), or the GEMM whose epilogue writes
-    K/V into the ring (rtv_qkv_gemm_append).  Inputs N(0,1) (W N(0, 1/6144)),
-    drawn on the device."""
+    K/V into the ring (rtv_qkv_gemm_append).  Also one GPU's share of the
+    out-projection (quantization and GEMM, O [11968 x 1536] to [11968 x 6144]).
+    Inputs N(0,1) (W N(0, 1/K)), drawn on the device."""
     import torch
 
     import kv_cache_attention_rtv_amd as rtv
@@ -328,6 +329,39 @@ def projection(args):
         "fused_frac_fp8_peak": round(flops / (t_fused * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
     }
     del cache, x, wt, xc, wc, qkv, q_out, ws
+
+    # One GPU's share of the out-projection, the GEMM whose partial sums a
+    # tensor-parallel group all-reduces after attention: the attention output
+    # of the step's 12 query heads (O [n x 1536] bf16) to e4m3, times Wo^T
+    # [6144 x 1536], to a partial [n x 6144] bf16 (the exchange itself needs
+    # more than one GPU)
+    step_wl = get_workload("step")
+    ko = step_wl.n_q_heads * step_wl.head_dim
+    o = device_normal_bf16((n, ko), (4, 0, 2), dev)
+    wot = (device_normal_bf16((hid, ko), (4, 0, 3), dev).float() * (1.0 / ko ** 0.5)).to(torch.bfloat16)
+    oc, so = rtv.quant_fp8_per_tensor(o)
+    woc, swo = rtv.quant_fp8_per_tensor(wot)
+    part = torch.empty((n, hid), dtype=torch.bfloat16, device=dev)
+    ws_o = torch.empty(rtv.abi.rtv_quant_workspace_bytes(o.numel()), dtype=torch.uint8, device=dev)
+
+    def quant_o():
+        rtv.quant_fp8_per_tensor(o, oc, so, ws_o)
+
+    def gemm_o():
+        rtv.gemm_fp8(oc, so, woc, swo, part)
+
+    t_quant_o = timed(quant_o)
+    t_gemm_o = timed(gemm_o)
+    flops_o = 2.0 * n * ko * hid
+    result["out_projection_share"] = {
+        "config": f"O [{n} x {ko}] bf16 ({step_wl.n_q_heads} query heads x {step_wl.head_dim}) to e4m3, "
+                  f"times Wo^T [{hid} x {ko}] e4m3, to a partial [{n} x {hid}] bf16 "
+                  f"({n * hid * 2 / 1e6:.1f} MB for the all-reduce, not run on one GPU)",
+        "quant_ms": round(t_quant_o, 4), "gemm_ms": round(t_gemm_o, 4),
+        "gemm_tflops": round(flops_o / (t_gemm_o * 1e-3) / 1e12, 1),
+        "gemm_frac_fp8_peak": round(flops_o / (t_gemm_o * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+    }
+    del o, wot, oc, woc, part, ws_o
     return result
 
 

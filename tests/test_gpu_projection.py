@@ -26,7 +26,7 @@ from oracle import rope as orope
 from oracle.cache import OracleKVCache
 from tests.gpu_helpers import attention_errors, bf16_to_np_f32, ring_rows, to_dev_bf16
 from workloads import get_workload, query_normal, qkv_normal
-from workloads.generate import projection_inputs
+from workloads.generate import out_projection_inputs, projection_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -221,6 +221,34 @@ def _check_rows_against_oracle(g_codes, g_scales, w_codes, w_scales, same_rows):
         wd = oquant.dequantize_rows(w_codes[d], w_scales[d])
         amax = np.maximum(np.abs(wd).max(axis=-1, keepdims=True), 1e-30)
         assert np.all(np.abs(gd - wd) <= 2.0 ** -3 * amax + 1e-30)
+
+
+def test_out_projection_share_sampled(rtv_lib):
+    """One GPU's share of the out-projection at its full size: the attention
+    output of 12 query heads, O [11968 x 1536], and Wo [1536 x 6144]; both
+    quantizations bit-exact in full, the GEMM (1128 tiles of 256 x 256: four
+    whole rounds and a last round in half tiles) on sampled rows."""
+    wl = get_workload("step")
+    n, ko, hid = wl.chunk_tokens, wl.n_q_heads * wl.head_dim, get_workload("proj").hidden
+    dev = torch.device("cuda")
+    o, w = out_projection_inputs(n, ko, hid)
+    print("out-projection share: quantize", flush=True)
+    oc, so = rtv_lib.quant_fp8_per_tensor(to_dev_bf16(o))
+    wtc, sw = rtv_lib.quant_fp8_per_tensor(to_dev_bf16(np.ascontiguousarray(w.T)))
+    want_oc, want_so = ogemm.quantize_per_tensor(obf16.to_f32(o))
+    want_wc, want_sw = ogemm.quantize_per_tensor(obf16.to_f32(w))
+    assert np.float32(so.item()).view(np.uint32) == np.float32(want_so).view(np.uint32)
+    assert np.float32(sw.item()).view(np.uint32) == np.float32(want_sw).view(np.uint32)
+    assert np.array_equal(oc.cpu().numpy(), want_oc)
+    assert np.array_equal(wtc.cpu().numpy(), want_wc.T)
+    print("out-projection share: gemm", flush=True)
+    out = rtv_lib.gemm_fp8(oc, so, wtc, sw)
+    assert tuple(out.shape) == (n, hid)
+    rng = np.random.default_rng(12)
+    # rows of the first tile, of the last whole round's tiles and of the half-tile round
+    rows = np.unique(np.concatenate([[0, 255, 256, 11775, 11776, n - 1], rng.integers(0, n, 40)]))
+    got = _np_bits(out[torch.as_tensor(rows, device=dev)])
+    _check_gemm(got, want_oc[rows], want_so, want_wc, want_sw)
 
 
 def test_projection_full_size_sampled(rtv_lib):

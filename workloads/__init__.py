@@ -11,6 +11,7 @@ from .generate import (
     f32_to_bf16_bits,
     qkv_normal,
     kv_student_t_outliers,
+    out_projection_inputs,
     projection_inputs,
     query_normal,
     seed_key,
@@ -24,6 +25,7 @@ __all__ = [
     "f32_to_bf16_bits",
     "qkv_normal",
     "kv_student_t_outliers",
+    "out_projection_inputs",
     "projection_inputs",
     "query_normal",
     "seed_key",

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import numpy as np
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_X, TENSOR_W = 0, 1, 2, 3, 4
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_X, TENSOR_W, TENSOR_O, TENSOR_WO = 0, 1, 2, 3, 4, 5, 6
 # keys for the per-layer choices of the stress workload
 _OUTLIER_CHANNELS, _ZERO_ROWS = 101, 102
 
@@ -99,6 +99,18 @@ def projection_inputs(wl, layer: int = 0, step: int = 0, seed: int = 0):
     w = rng.standard_normal((wl.hidden, wl.proj_width), dtype=np.float32)
     w *= np.float32(1.0 / np.sqrt(wl.hidden))
     return x, f32_to_bf16_bits(w)
+
+
+def out_projection_inputs(n_tokens: int, in_cols: int, hidden: int, layer: int = 0, step: int = 0, seed: int = 0):
+    """One GPU's share of the out-projection: O [n_tokens, in_cols] ~ N(0,1) (the
+    attention output of its query heads) and Wo [in_cols, hidden] ~ N(0, 1/in_cols),
+    both rounded to bf16."""
+    rng = np.random.default_rng(seed_key(seed, layer, step, 0, TENSOR_O))
+    o = f32_to_bf16_bits(rng.standard_normal((n_tokens, in_cols), dtype=np.float32))
+    rng = np.random.default_rng(seed_key(seed, layer, 0, 0, TENSOR_WO))
+    w = rng.standard_normal((in_cols, hidden), dtype=np.float32)
+    w *= np.float32(1.0 / np.sqrt(in_cols))
+    return o, f32_to_bf16_bits(w)
 
 
 def device_normal_bf16(shape, seed_tuple, device):
