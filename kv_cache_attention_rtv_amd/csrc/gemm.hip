@@ -11,9 +11,11 @@
 // GEMM decomposition: one workgroup = a 256 x 256 tile of C, 16 waves in a
 // 4 (M) x 4 (N) grid, each wave 64 x 64 = 2 x 2 blocks of
 // v_mfma_f32_32x32x64_f8f6f4 (four waves per SIMD, so that one wave's
-// operand reads and barrier waits overlap the others' products).  The Bt block is the MFMA A operand and the A
-// block the B operand, so a lane of the result holds four consecutive output
-// columns of one row (one 8-byte bf16 store).  K advances 128 bytes per stage
+// operand reads and barrier waits overlap the others' products).  The Bt
+// block is the MFMA A operand and the A block the B operand, so a lane of
+// the result holds four consecutive output columns of one row; the plain
+// GEMM passes the tile through LDS as bf16 and writes it in whole rows, 16
+// bytes per lane.  K advances 128 bytes per stage
 // through two LDS stages (rows padded to 144 B, conflict-free 16-byte reads);
 // the global loads of stage t+1 are in flight while stage t is computed.
 // Tiles are numbered XCD-aware (each XCD walks a contiguous range) and grouped
@@ -165,7 +167,7 @@ struct GemmArgs {
   int32_t n_mt, n_nt, n_tiles;
   int32_t tile_base;   // first logical tile of the launch
   int32_t n_launch;    // work items of the launch (tiles, or half tiles)
-  int32_t vec_store;   // 8-byte stores allowed (c 8-aligned, ldc % 4 == 0)
+  int32_t vec_store;   // 16-byte stores allowed (c 16-aligned, ldc % 8 == 0)
   // fused QKV epilogue: columns [0, q_cols) are Q (bf16 into c), then
   // n_kv_heads K heads and n_kv_heads V heads of D columns into the ring
   int32_t q_cols;
@@ -429,31 +431,45 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
     fused_epilogue<FUSED_D, BN>(g, acc, s, smem, m0, n0, wm, wn, wave, lane);
     return;
   }
+  // The tile goes through LDS as bf16 (the operand stages are free once every
+  // wave has left the loop), so that it leaves in whole rows: each store
+  // instruction writes two 512-byte runs (16 bytes per lane) instead of 32
+  // rows of 16 bytes.
+  constexpr int kOutRow = BN * 2 + 16;          // bytes per tile row in LDS (padded)
+  static_assert(kBM * kOutRow <= 2 * kStageBytes, "the bf16 tile fits the operand stages");
   const int hh = lane >> 5;
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int m = m0 + wm + 32 * i + (lane & 31);
-    if (m >= g.M) continue;
-    uint16_t* crow = g.c + (int64_t)m * g.ldc;
+    const int row = wm + 32 * i + (lane & 31);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int grp4 = 0; grp4 < 4; ++grp4) {
-        const int n = n0 + wn + 32 * j + 8 * grp4 + 4 * hh;
-        const float v0 = acc[i][j][4 * grp4 + 0] * s, v1 = acc[i][j][4 * grp4 + 1] * s;
-        const float v2 = acc[i][j][4 * grp4 + 2] * s, v3 = acc[i][j][4 * grp4 + 3] * s;
-        if (g.vec_store && n + 4 <= g.N) {
-          uint2 o;
-          o.x = pack_bf16x2(v0, v1);
-          o.y = pack_bf16x2(v2, v3);
-          *reinterpret_cast<uint2*>(crow + n) = o;
-        } else {
-          const float vs[4] = {v0, v1, v2, v3};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < g.N) crow[n + e] = (uint16_t)f32_to_bf16_bits(vs[e]);
-        }
+        const int col = wn + 32 * j + 8 * grp4 + 4 * hh;
+        const auto& a4 = acc[i][j];
+        *reinterpret_cast<uint2*>(smem + row * kOutRow + col * 2) =
+            make_uint2(pack_bf16x2(a4[4 * grp4] * s, a4[4 * grp4 + 1] * s),
+                       pack_bf16x2(a4[4 * grp4 + 2] * s, a4[4 * grp4 + 3] * s));
       }
+  }
+  __syncthreads();
+  constexpr int kRowChunks = BN * 2 / 16;       // 16-byte chunks per tile row
+#pragma unroll
+  for (int c = threadIdx.x; c < kBM * kRowChunks; c += kGemmThreads) {
+    const int row = c / kRowChunks;
+    const int n = n0 + (c % kRowChunks) * 8;
+    const int m = m0 + row;
+    if (m >= g.M || n >= g.N) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(smem + row * kOutRow + (c % kRowChunks) * 16);
+    uint16_t* dst = g.c + (int64_t)m * g.ldc + n;
+    if (g.vec_store && n + 8 <= g.N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < g.N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
     }
   }
 }
@@ -522,7 +538,7 @@ static GemmArgs gemm_args(const uint8_t* a, const float* sa, const uint8_t* bt, 
   g.n_mt = (M + kBM - 1) / kBM;
   g.n_nt = (N + kBN - 1) / kBN;
   g.n_tiles = g.n_mt * g.n_nt;
-  g.vec_store = (reinterpret_cast<uintptr_t>(c) % 8 == 0) && (ldc % 4 == 0);
+  g.vec_store = (reinterpret_cast<uintptr_t>(c) % 16 == 0) && (ldc % 8 == 0);
   return g;
 }
 
