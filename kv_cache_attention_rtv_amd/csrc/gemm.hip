@@ -27,7 +27,8 @@
 //
 // Fused QKV epilogue (gemm_fp8_kernel<D>, D = head_dim): the output columns
 // are [Q heads | K heads | V heads] of one chunk's tokens.  Q columns are
-// written as bf16 like the plain GEMM; K and V heads never reach HBM in bf16:
+// written as bf16 like the plain GEMM (tiles of Q columns only take the plain
+// GEMM's epilogue); K and V heads never reach HBM in bf16:
 // from the f32 result (times s_a s_b) the epilogue applies RoPE to K at the
 // chunk's positions and quantizes each (token, head) row to e4m3 with the
 // cache's row rule, straight into the ring slots of the current chunk (the
@@ -428,8 +429,12 @@ __global__ void __launch_bounds__(kGemmThreads, 1) gemm_fp8_kernel(GemmArgs g) {
   // n = n0+wn+32j + 8(r/4) + 4(lane/32) + r%4
   const float s = (*g.sa) * (*g.sb);
   if constexpr (FUSED_D > 0) {
-    fused_epilogue<FUSED_D, BN>(g, acc, s, smem, m0, n0, wm, wn, wave, lane);
-    return;
+    // tiles with K or V columns take the fused epilogue; tiles of Q columns
+    // only are plain bf16 and leave like the plain GEMM's
+    if (n0 + BN > g.q_cols) {
+      fused_epilogue<FUSED_D, BN>(g, acc, s, smem, m0, n0, wm, wn, wave, lane);
+      return;
+    }
   }
   // The tile goes through LDS as bf16 (the operand stages are free once every
   // wave has left the loop), so that it leaves in whole rows: each store
