@@ -172,9 +172,11 @@ def test_gemm_round_structure(rtv_lib, M, N, K):
     _check_gemm(got, a[rows], sa, bt.T, sb, min_same=0.9)
 
 
-def test_gemm_strided_output_and_errors(rtv_lib):
+@pytest.mark.parametrize("ldc", [77,    # odd row stride: element stores
+                                 80])   # 16-byte rows: vector stores, the last 6 columns of a row by element
+def test_gemm_strided_output_and_errors(rtv_lib, ldc):
     rng = np.random.default_rng(5)
-    M, N, K, ldc = 130, 70, 128, 77         # odd row stride: element stores
+    M, N, K = 130, 70, 128
     a, bt = _random_codes(rng, (M, K)), _random_codes(rng, (N, K))
     dev = torch.device("cuda")
     big = torch.full((M, ldc), 7, dtype=torch.int16, device=dev).view(torch.bfloat16)
