@@ -724,6 +724,11 @@ def main():
         "achieved": round(ref_bytes / (ref_avg * 1e-3) / 1e9, 1),
         "frac": round(ref_bytes / (ref_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "append_time_over_reference": round(app_avg_ms / ref_avg, 3),
+        # the two move different bytes: the append's rate over the reference's,
+        # counting the append's algorithmic bytes and the chunk's RoPE table
+        # rows (n x D floats), which it must read
+        "append_rate_over_reference": round(
+            ((app_bytes + n * wl.head_dim * 4) / app_avg_ms) / (ref_bytes / ref_avg), 3),
     }
     del ref_out
     if args.copy_calibration:
