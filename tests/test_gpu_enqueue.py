@@ -11,7 +11,9 @@ the GPU is still busy with the step (the stream is not idle right after the
 last call), and the host time of the enqueue must be a small fraction of the
 GPU time of the step.  A call that synchronized would make the first check
 fail; one that waited on the GPU in any other way would make its host time
-grow towards the GPU time.
+grow towards the GPU time.  Both ring-state modes: host state, and device
+state (the mode a captured step runs in, where the calls read and move the
+ring state in their kernels).
 """
 import time
 
@@ -27,7 +29,8 @@ N_LAYERS = 8
 CALLS = 4
 
 
-def test_step_calls_only_enqueue(rtv_lib):
+@pytest.mark.parametrize("device_state", [False, True])
+def test_step_calls_only_enqueue(rtv_lib, device_state):
     rtv = rtv_lib
     wl = get_workload("step")
     dev = torch.device("cuda:0")
@@ -55,10 +58,12 @@ def test_step_calls_only_enqueue(rtv_lib):
         step()
     torch.cuda.synchronize()
     assert cache.window(0).window_frames == wl.capacity_frames
+    if device_state:
+        cache.device_state_begin(stream=stream)    # (synchronizes, once)
 
     results = []
     for rep in range(3):
-        print(f"enqueue: timed step {rep}", flush=True)
+        print(f"enqueue: device_state={device_state} timed step {rep}", flush=True)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         t0 = time.perf_counter()
@@ -71,6 +76,8 @@ def test_step_calls_only_enqueue(rtv_lib):
         results.append((t1 - t0, gpu_s, busy))
         print(f"  host enqueue {1e3 * (t1 - t0):.3f} ms, GPU {1e3 * gpu_s:.3f} ms, "
               f"stream busy after the last call: {busy}")
+    if device_state:
+        cache.device_state_end(stream=stream)
     for host_s, gpu_s, busy in results:
         assert busy, "the stream was idle when the calls returned: a call waited for the GPU"
         assert host_s < 0.25 * gpu_s, (host_s, gpu_s)
