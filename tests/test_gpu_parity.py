@@ -204,6 +204,13 @@ def test_state_errors(rtv_lib):
     assert e.value.status == abi.RTV_ERR_STATE
     L = gpu.layout(0)
     assert L.next_global_frame == 2 * wl.chunk_frames and L.appended == 0
+    # calls after the cache is destroyed reach the library with no handle
+    gpu.close()
+    for call in (lambda: gpu.append(0, kd, vd), lambda: gpu.attend(0, qd), lambda: gpu.advance(0),
+                 lambda: gpu.layout(0)):
+        with pytest.raises(rtv_lib.RtvError) as e:
+            call()
+        assert e.value.status == abi.RTV_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("T,F,C,D,H,Hq,steps", [
